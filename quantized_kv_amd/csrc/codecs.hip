@@ -1,0 +1,277 @@
+// Codec kernels: signed-Hadamard + MXFP8 (E4M3 elements, E8M0 block exponent, 32-element blocks)
+// and grouped 4-bit K/V with a float32 recent window.
+//
+// MXFP8: "Catnip Week 10 KV Cache Attention Study", experiment design step 4 (signed-H128 +
+// physical E4M3/E8M0 K32 Q/K) and the section on Q/K and probability quantization.
+// Int4 KV: "KV residual window" (huhohoo.com), sections on the fixed budget (group 32, K per channel
+// over token groups, V per token over feature groups, R in {0, 16, 64}) and on the payload.
+//
+// Both codecs are exact specifications: the codes and scale bytes are reproduced bit for bit, so the
+// arithmetic below is fixed (float64 sums, float32 IEEE operations, round to nearest even).
+#include "kvprof_internal.h"
+#include "kvprof_device.h"
+
+namespace kvp {
+namespace {
+
+// One 64-lane block per row (grid-stride over rows). The rotation runs as a Walsh-Hadamard
+// butterfly on float64 values in LDS; sums of bf16 inputs are exact, so the butterfly order does not
+// change the result.
+__global__ __launch_bounds__(64) void pack_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                        int d, const int8_t* __restrict__ signs,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+  __shared__ double buf[256];
+  __shared__ float yv[256];
+  __shared__ int bexp[8];
+  const int lane = threadIdx.x;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const uint16_t* xr = x + r * d;
+    for (int c = lane; c < d; c += 64) {
+      double v = (double)bf16_to_f32(xr[c]);
+      buf[c] = signs ? v * (double)signs[c] : v;
+    }
+    __syncthreads();
+    if (signs) {
+      for (int h = 1; h < d; h <<= 1) {
+        for (int b = lane; b < d / 2; b += 64) {
+          int i = (b / h) * 2 * h + (b % h);
+          double a0 = buf[i], a1 = buf[i + h];
+          buf[i] = a0 + a1;
+          buf[i + h] = a0 - a1;
+        }
+        __syncthreads();
+      }
+      const double c = (d == 128) ? kInvSqrt128 : 1.0 / sqrt((double)d);
+      for (int i = lane; i < d; i += 64) {
+        double t = __dmul_rn(buf[i], c);  // rounded to float64, then to float32 below
+        yv[i] = (float)t;
+      }
+    } else {
+      for (int i = lane; i < d; i += 64) yv[i] = (float)buf[i];
+    }
+    __syncthreads();
+    const int nb = d / 32;
+    if (lane < nb) {
+      float amax = 0.f;
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(yv[lane * 32 + i]));
+      int e = e8m0_exp(amax);
+      bexp[lane] = e;
+      scales[r * nb + lane] = (uint8_t)(e + 127);
+    }
+    __syncthreads();
+    for (int i = lane; i < d; i += 64) {
+      float sv = ldexpf(yv[i], -bexp[i / 32]);
+      codes[r * d + i] = e4m3_rne(sv);
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void unpack_mxfp8_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                    int64_t n, int d, float* __restrict__ out_f32,
+                                    uint16_t* __restrict__ out_bf16) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t r = i / d;
+    int c = (int)(i - r * d);
+    int e = (int)scales[r * (d / 32) + c / 32] - 127;
+    float v = ldexpf(e4m3_value(codes[i]), e);
+    if (out_f32) out_f32[i] = v;
+    if (out_bf16) out_bf16[i] = (uint16_t)(__float_as_uint(v) >> 16);  // exact: <= 4 significant bits
+  }
+}
+
+// ---- grouped 4-bit K/V ---------------------------------------------------------------------------
+
+// Asymmetric 4-bit code of x in a group with min/max lo/hi: every operation is an IEEE float32
+// operation with round to nearest even (no contraction: there is no multiply to fuse).
+struct Int4Meta {
+  _Float16 s, m;
+};
+__device__ __forceinline__ Int4Meta int4_meta(float lo, float hi) {
+  float scale32 = __fdiv_rn(__fsub_rn(hi, lo), 15.0f);
+  Int4Meta mt;
+  mt.s = (_Float16)scale32;
+  mt.m = (_Float16)lo;
+  return mt;
+}
+__device__ __forceinline__ uint32_t int4_code(float x, Int4Meta mt) {
+  float s = (float)mt.s;
+  if (s == 0.f) return 0;
+  float q = __builtin_rintf(__fdiv_rn(__fsub_rn(x, (float)mt.m), s));
+  q = fminf(fmaxf(q, 0.f), 15.f);
+  return (uint32_t)q;
+}
+
+// K: one thread per (head, token group, channel pair).
+__global__ void pack_k_kernel(const uint16_t* __restrict__ k, int heads, int64_t N, int d, int R,
+                              uint8_t* __restrict__ out, size_t blob) {
+  Int4Layout L = int4_layout(N, d, R);
+  int64_t total = (int64_t)heads * L.G * (d / 2);
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    int cp = (int)(t % (d / 2));
+    int64_t g = (t / (d / 2)) % L.G;
+    int h = (int)(t / ((d / 2) * L.G));
+    const uint16_t* kh = k + (int64_t)h * N * d;
+    uint8_t* ob = out + (size_t)h * blob;
+    int64_t t0 = g * 32, t1 = min(t0 + 32, L.n);
+    Int4Meta mt[2];
+    for (int q = 0; q < 2; ++q) {
+      int c = 2 * cp + q;
+      float lo = INFINITY, hi = -INFINITY;
+      for (int64_t tok = t0; tok < t1; ++tok) {
+        float xv = bf16_to_f32(kh[tok * d + c]);
+        lo = fminf(lo, xv);
+        hi = fmaxf(hi, xv);
+      }
+      mt[q] = int4_meta(lo, hi);
+      _Float16* meta = reinterpret_cast<_Float16*>(ob + L.km) + (g * d + c) * 2;
+      meta[0] = mt[q].s;
+      meta[1] = mt[q].m;
+    }
+    for (int64_t tok = t0; tok < g * 32 + 32; ++tok) {
+      uint32_t byte = 0;
+      if (tok < t1) {
+        byte = int4_code(bf16_to_f32(kh[tok * d + 2 * cp]), mt[0]) |
+               (int4_code(bf16_to_f32(kh[tok * d + 2 * cp + 1]), mt[1]) << 4);
+      }
+      ob[L.kc + tok * (d / 2) + cp] = (uint8_t)byte;
+    }
+  }
+}
+
+// V: one thread per (head, token, 32-feature group).
+__global__ void pack_v_kernel(const uint16_t* __restrict__ v, int heads, int64_t N, int d, int R,
+                              uint8_t* __restrict__ out, size_t blob) {
+  Int4Layout L = int4_layout(N, d, R);
+  const int nfg = d / 32;
+  int64_t total = (int64_t)heads * L.n * nfg;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    int f = (int)(t % nfg);
+    int64_t tok = (t / nfg) % L.n;
+    int h = (int)(t / (nfg * L.n));
+    const uint16_t* xr = v + ((int64_t)h * N + tok) * d + f * 32;
+    uint8_t* ob = out + (size_t)h * blob;
+    float lo = INFINITY, hi = -INFINITY;
+    for (int c = 0; c < 32; ++c) {
+      float xv = bf16_to_f32(xr[c]);
+      lo = fminf(lo, xv);
+      hi = fmaxf(hi, xv);
+    }
+    Int4Meta mt = int4_meta(lo, hi);
+    _Float16* meta = reinterpret_cast<_Float16*>(ob + L.vm) + (tok * nfg + f) * 2;
+    meta[0] = mt.s;
+    meta[1] = mt.m;
+    for (int c = 0; c < 32; c += 2) {
+      uint32_t byte = int4_code(bf16_to_f32(xr[c]), mt) | (int4_code(bf16_to_f32(xr[c + 1]), mt) << 4);
+      ob[L.vc + tok * (d / 2) + (f * 32 + c) / 2] = (uint8_t)byte;
+    }
+  }
+}
+
+// Header and the float32 residual window (bf16 -> fp32 is exact).
+__global__ void pack_tail_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                 int heads, int64_t N, int d, int R, uint8_t* __restrict__ out,
+                                 size_t blob) {
+  Int4Layout L = int4_layout(N, d, R);
+  int64_t per = (int64_t)R * d;
+  int64_t total = (int64_t)heads * (per + 1);
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    int h = (int)(t / (per + 1));
+    int64_t e = t % (per + 1);
+    uint8_t* ob = out + (size_t)h * blob;
+    if (e == per) {
+      int32_t* hd = reinterpret_cast<int32_t*>(ob);
+      hd[0] = (int32_t)N;
+      hd[1] = d;
+      hd[2] = R;
+      hd[3] = 32;
+      continue;
+    }
+    int64_t src = ((int64_t)h * N + L.n) * d + e;
+    reinterpret_cast<float*>(ob + L.kr)[e] = bf16_to_f32(k[src]);
+    reinterpret_cast<float*>(ob + L.vr)[e] = bf16_to_f32(v[src]);
+  }
+}
+
+__global__ void unpack_int4_kernel(const uint8_t* __restrict__ packed, int heads, int64_t N, int d,
+                                   int R, size_t blob, float* __restrict__ k_out,
+                                   float* __restrict__ v_out) {
+  Int4Layout L = int4_layout(N, d, R);
+  int64_t total = (int64_t)heads * N * d;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    int c = (int)(t % d);
+    int64_t tok = (t / d) % N;
+    int h = (int)(t / (d * N));
+    const uint8_t* b = packed + (size_t)h * blob;
+    float kv, vv;
+    if (tok < L.n) {
+      int g = (int)(tok / 32);
+      const _Float16* km = reinterpret_cast<const _Float16*>(b + L.km) + ((int64_t)g * d + c) * 2;
+      uint32_t kc = (b[L.kc + tok * (d / 2) + c / 2] >> ((c & 1) * 4)) & 0xF;
+      kv = fmaf((float)kc, (float)km[0], (float)km[1]);
+      const _Float16* vm = reinterpret_cast<const _Float16*>(b + L.vm) + (tok * (d / 32) + c / 32) * 2;
+      uint32_t vc = (b[L.vc + tok * (d / 2) + c / 2] >> ((c & 1) * 4)) & 0xF;
+      vv = fmaf((float)vc, (float)vm[0], (float)vm[1]);
+    } else {
+      kv = reinterpret_cast<const float*>(b + L.kr)[(tok - L.n) * d + c];
+      vv = reinterpret_cast<const float*>(b + L.vr)[(tok - L.n) * d + c];
+    }
+    k_out[t] = kv;
+    v_out[t] = vv;
+  }
+}
+
+inline unsigned grid_for(int64_t n, int block, unsigned cap = 65536) {
+  int64_t g = (n + block - 1) / block;
+  if (g < 1) g = 1;
+  return (unsigned)(g > cap ? cap : g);
+}
+
+}  // namespace
+
+hipError_t launch_pack_mxfp8(const uint16_t* x, int64_t rows, int d, const int8_t* signs,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  unsigned g = (unsigned)(rows < 65536 * 4 ? rows : 65536 * 4);
+  hipLaunchKernelGGL(pack_mxfp8_kernel, dim3(g), dim3(64), 0, s, x, rows, d, signs, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int d,
+                               float* out_f32, uint16_t* out_bf16, hipStream_t s) {
+  int64_t n = rows * d;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(unpack_mxfp8_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, codes, scales, n,
+                     d, out_f32, out_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_int4kv(const uint16_t* k, const uint16_t* v, int heads, int64_t N, int d,
+                              int R, uint8_t* out, size_t blob, hipStream_t s) {
+  if (heads == 0) return hipSuccess;
+  Int4Layout L = int4_layout(N, d, R);
+  int64_t nk = (int64_t)heads * L.G * (d / 2);
+  int64_t nv = (int64_t)heads * L.n * (d / 32);
+  int64_t nt = (int64_t)heads * ((int64_t)R * d + 1);
+  if (nk > 0) hipLaunchKernelGGL(pack_k_kernel, dim3(grid_for(nk, 128)), dim3(128), 0, s, k, heads, N, d, R, out, blob);
+  if (nv > 0) hipLaunchKernelGGL(pack_v_kernel, dim3(grid_for(nv, 128)), dim3(128), 0, s, v, heads, N, d, R, out, blob);
+  hipLaunchKernelGGL(pack_tail_kernel, dim3(grid_for(nt, 256)), dim3(256), 0, s, k, v, heads, N, d, R, out, blob);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_int4kv(const uint8_t* packed, int heads, int64_t N, int d, int R,
+                                size_t blob, float* k_out, float* v_out, hipStream_t s) {
+  int64_t n = (int64_t)heads * N * d;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(unpack_int4_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, packed, heads, N, d,
+                     R, blob, k_out, v_out);
+  return hipGetLastError();
+}
+
+}  // namespace kvp

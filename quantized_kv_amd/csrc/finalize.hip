@@ -1,0 +1,177 @@
+// Per-record aggregation and output comparison kernels.
+//
+// Heatmap: "Catnip Week 10 KV Cache Attention Study", Figure 2 — the 6x16 temporal map, each query
+// frame's 16 key-frame masses averaged over its sampled rows (rows sum to 100 %), and the per-layer
+// maps of Figure 8. Histograms: the distributions of support and region mass over the rows of a record
+// (Figure 5). Comparison: "KV residual window" (relative L2 of the attention output) and the
+// MiniCPM5-2B predictor study, section 0 (recall@32).
+#include "kvprof_internal.h"
+
+namespace kvp {
+namespace {
+
+// One thread per (batch, head, group, frame): mean over the rows of that group, in row order.
+__global__ void heatmap_kernel(const float* __restrict__ fm, const int* __restrict__ row_group,
+                               int n_batch, int hq, int nq, int ng, int nf, float* __restrict__ hm) {
+  long long total = (long long)n_batch * hq * ng * nf;
+  for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
+       t += (long long)gridDim.x * blockDim.x) {
+    int f = (int)(t % nf);
+    int gq = (int)((t / nf) % ng);
+    long long bh = t / ((long long)nf * ng);
+    const float* base = fm + bh * nq * nf;
+    float s = 0.f;
+    int cnt = 0;
+    for (int i = 0; i < nq; ++i) {
+      if (row_group[i] == gq) {
+        s += base[(long long)i * nf + f];
+        ++cnt;
+      }
+    }
+    hm[t] = cnt ? s / (float)cnt : 0.f;
+  }
+}
+
+// Mean over the query heads of each (batch, group, frame), in head order.
+__global__ void heatmap_mean_kernel(const float* __restrict__ hm, int n_batch, int hq, int ng, int nf,
+                                    float* __restrict__ out) {
+  long long total = (long long)n_batch * ng * nf;
+  for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
+       t += (long long)gridDim.x * blockDim.x) {
+    long long b = t / ((long long)ng * nf);
+    long long gf = t % ((long long)ng * nf);
+    float s = 0.f;
+    for (int h = 0; h < hq; ++h) s += hm[(b * hq + h) * ng * nf + gf];
+    out[t] = s / (float)hq;
+  }
+}
+
+__device__ __forceinline__ int bin100(float x, int bins) {
+  int bn = (int)floorf(x * (float)bins);
+  return bn < 0 ? 0 : (bn >= bins ? bins - 1 : bn);
+}
+
+// One thread per row: integer atomics, so the counts are independent of the order.
+__global__ void hist_kernel(const float* __restrict__ support, const float* __restrict__ region,
+                            int n_batch, int rows_per_b, int nreg, int bins, unsigned* __restrict__ hist) {
+  long long total = (long long)n_batch * rows_per_b;
+  for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
+       t += (long long)gridDim.x * blockDim.x) {
+    long long b = t / rows_per_b;
+    unsigned* hb = hist + b * (long long)(1 + nreg) * bins;
+    atomicAdd(&hb[bin100(support[t], bins)], 1u);
+    for (int q = 0; q < nreg; ++q) atomicAdd(&hb[(1 + q) * bins + bin100(region[t * nreg + q], bins)], 1u);
+  }
+}
+
+__global__ void zero_u32_kernel(unsigned* p, long long n) {
+  for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < n;
+       t += (long long)gridDim.x * blockDim.x)
+    p[t] = 0u;
+}
+
+// One wave per row: squared norms in float64, recall from the two index lists.
+__global__ __launch_bounds__(64) void compare_kernel(const float* __restrict__ oq, const float* __restrict__ oref,
+                                                     const int* __restrict__ tq, const int* __restrict__ tref,
+                                                     long long rows, int d, float* __restrict__ rel,
+                                                     float* __restrict__ recall, double* __restrict__ part) {
+  const int lane = threadIdx.x;
+  for (long long rrow = blockIdx.x; rrow < rows; rrow += gridDim.x) {
+    double dd = 0.0, nn = 0.0;
+    for (int c = lane; c < d; c += 64) {
+      double a = oq[rrow * d + c], bb = oref[rrow * d + c];
+      dd += (a - bb) * (a - bb);
+      nn += bb * bb;
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+      dd += __shfl_xor(dd, o);
+      nn += __shfl_xor(nn, o);
+    }
+    int hit = 0;
+    if (tq && tref && lane < 32) {
+      int x = tq[rrow * 32 + lane];
+      if (x >= 0)
+        for (int q = 0; q < 32; ++q) hit += (tref[rrow * 32 + q] == x);
+    }
+    for (int o = 32; o >= 1; o >>= 1) hit += __shfl_xor(hit, o);
+    if (lane == 0) {
+      rel[rrow] = (float)(nn > 0 ? sqrt(dd / nn) : 0.0);
+      if (recall) recall[rrow] = (float)hit / 32.f;
+      part[2 * rrow] = dd;
+      part[2 * rrow + 1] = nn;
+    }
+  }
+}
+
+// Single block: sums of the per-row partials in row order (deterministic).
+__global__ __launch_bounds__(256) void compare_sum_kernel(const double* __restrict__ part, long long rows,
+                                                          double* __restrict__ sums) {
+  __shared__ double sd[256], sn[256];
+  const int t = threadIdx.x;
+  long long per = (rows + 255) / 256;
+  double a = 0.0, b = 0.0;
+  for (long long i = t * per; i < (t + 1) * per && i < rows; ++i) {
+    a += part[2 * i];
+    b += part[2 * i + 1];
+  }
+  sd[t] = a;
+  sn[t] = b;
+  __syncthreads();
+  if (t == 0) {
+    double x = 0.0, y = 0.0;
+    for (int i = 0; i < 256; ++i) {
+      x += sd[i];
+      y += sn[i];
+    }
+    sums[0] = x;
+    sums[1] = y;
+  }
+}
+
+inline unsigned grid_for(long long n, int block) {
+  long long g = (n + block - 1) / block;
+  if (g < 1) g = 1;
+  return (unsigned)(g > 65536 ? 65536 : g);
+}
+
+}  // namespace
+
+hipError_t launch_heatmap(const float* frame_mass, const int* row_group, int n_batch, int hq, int nq,
+                          int n_groups, int n_frames, float* heatmap, float* heatmap_mean,
+                          hipStream_t s) {
+  long long n = (long long)n_batch * hq * n_groups * n_frames;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(heatmap_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, frame_mass, row_group,
+                     n_batch, hq, nq, n_groups, n_frames, heatmap);
+  if (heatmap_mean) {
+    long long m = (long long)n_batch * n_groups * n_frames;
+    hipLaunchKernelGGL(heatmap_mean_kernel, dim3(grid_for(m, 256)), dim3(256), 0, s, heatmap, n_batch,
+                       hq, n_groups, n_frames, heatmap_mean);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_hist(const float* support, const float* region_mass, int n_batch, int rows_per_b,
+                       int n_regions, int bins, unsigned* hist, hipStream_t s) {
+  long long nh = (long long)n_batch * (1 + n_regions) * bins;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(grid_for(nh, 256)), dim3(256), 0, s, hist, nh);
+  long long n = (long long)n_batch * rows_per_b;
+  if (n > 0)
+    hipLaunchKernelGGL(hist_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, support, region_mass,
+                       n_batch, rows_per_b, n_regions, bins, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_compare(const float* oq, const float* oref, const int* tq, const int* tref,
+                          int64_t rows, int d, float* rel_row, float* recall_row, double* sums,
+                          hipStream_t s) {
+  // the per-row partials live in the sums buffer's tail: sums[2 + 2*rows]
+  if (rows == 0) return hipSuccess;
+  double* part = sums + 2;
+  hipLaunchKernelGGL(compare_kernel, dim3(grid_for(rows, 1)), dim3(64), 0, s, oq, oref, tq, tref,
+                     (long long)rows, d, rel_row, recall_row, part);
+  hipLaunchKernelGGL(compare_sum_kernel, dim3(1), dim3(256), 0, s, part, (long long)rows, sums);
+  return hipGetLastError();
+}
+
+}  // namespace kvp

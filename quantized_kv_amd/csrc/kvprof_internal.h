@@ -1,0 +1,85 @@
+// Internal declarations shared by the HIP translation units of libkvprof (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvprof.h"
+
+namespace kvp {
+
+// ---- launch wrappers (each returns hipSuccess or the launch error) ------------------------------
+
+hipError_t launch_pack_mxfp8(const uint16_t* x, int64_t rows, int d, const int8_t* signs,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_unpack_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int d,
+                               float* out_f32, uint16_t* out_bf16, hipStream_t s);
+hipError_t launch_pack_int4kv(const uint16_t* k, const uint16_t* v, int heads, int64_t N, int d,
+                              int R, uint8_t* out, size_t blob_bytes, hipStream_t s);
+hipError_t launch_unpack_int4kv(const uint8_t* packed, int heads, int64_t N, int d, int R,
+                                size_t blob_bytes, float* k_out, float* v_out, hipStream_t s);
+
+// Segments: the union of region and frame boundaries, clipped to [0, n_k]. Per-row segment masses
+// are the primitive the kernel reduces; region and frame masses are sums of segments.
+constexpr int kMaxSeg = 80;
+constexpr int kSegPerWave = 8;  // segments one wave's key range may overlap
+
+struct RowStatsParams {
+  // shapes
+  int n_batch, n_heads_q, n_heads_kv, n_q, n_k;
+  int group;  // n_heads_q / n_heads_kv
+  int rows_per_kv;  // group * n_q
+  int causal;
+  long long q_pos0;
+  float scale_log2;  // scale * log2(e)
+  // score source
+  const uint16_t* q;  // bf16 [b][hq][nq][128] (MX mode: dequantized MX values as bf16)
+  const uint16_t* k;  // bf16 [b][hkv][nk][128]
+  const uint16_t* v;
+  const uint8_t* kv_packed;  // INT4 mode
+  size_t blob_bytes;
+  int r_window;
+  const float* key_bias;
+  // reference stream for MX mode (unrotated bf16)
+  const uint16_t* q_ref;
+  const uint16_t* k_ref;
+  // segments
+  int n_seg;
+  int seg_bounds[kMaxSeg + 1];
+  signed char seg_region[kMaxSeg];  // region of the segment or -1
+  signed char seg_frame[kMaxSeg];   // frame of the segment or -1
+  int n_regions, n_frames;
+  // outputs
+  float* support;
+  float* top_mass;
+  int* top32;
+  int* strict_zero;
+  float* region_mass;
+  float* frame_mass;
+  float* row_max;
+  float* row_lse;
+  float* o;
+  float* tv_qk;
+  int* argmax;
+  int* argmax_ref;
+  float* p_zero_frac;
+  float* tv_p;
+  float* p_rowsum;
+};
+
+enum KSrc { KSRC_BF16 = 0, KSRC_INT4 = 1 };
+
+// Main row kernel. tpw = 16-key tiles per wave (16 waves per workgroup, 16 rows per workgroup).
+hipError_t launch_row_stats(const RowStatsParams& p, int tpw, int ksrc, bool mx, hipStream_t s);
+int row_stats_tpw_for(int n_k, bool mx);  // tiles per wave this build uses for n_k keys, or -1
+
+hipError_t launch_heatmap(const float* frame_mass, const int* row_group, int n_batch, int hq,
+                          int nq, int n_groups, int n_frames, float* heatmap, float* heatmap_mean,
+                          hipStream_t s);
+hipError_t launch_hist(const float* support, const float* region_mass, int n_batch, int rows_per_b,
+                       int n_regions, int bins, unsigned* hist, hipStream_t s);
+hipError_t launch_compare(const float* oq, const float* oref, const int* tq, const int* tref,
+                          int64_t rows, int d, float* rel_row, float* recall_row, double* sums,
+                          hipStream_t s);
+
+}  // namespace kvp

@@ -1,0 +1,1129 @@
+// Row kernel of the KV-cache attention row profiler.
+//
+// One workgroup = 8 waves = 16 query rows (the 16 columns of a 16x16 MFMA tile) of one (batch,
+// KV head). Wave w owns keys [w*TPW*16, (w+1)*TPW*16). The whole score row of every query stays on
+// chip: each lane holds one row's scores for 4 keys of each of its TPW tiles, as produced by the MFMA
+// S^T = K Q^T (lane l: query row l%16, keys 4*(l/16)+i of the tile). Every statistic is then a pass
+// over registers, with cross-lane / cross-wave reductions in a fixed order (bitwise deterministic):
+//
+//   A  scores u = (scale q.k + b) log2(e) on bf16 / f16 MFMA; row max and min
+//   B  e' = 2^(u - max + 64) (offset keeps strict-zero decisions in the normal float range);
+//      Z', sum e'(u - max + 64) for the entropy; per-segment masses (regions and key frames)
+//   C  256-bin histogram of D = bits(e'max) - bits(e') (monotone in e'), counts and fixed-point masses
+//   D  exact selection of four ranks (top-32 boundary, top-1/5/10 %): boundary bins are refined by
+//      further radix levels on the 48-bit key (D, key index) until at most 256 candidates remain,
+//      which are ranked exactly in LDS
+//   E  outputs; optional O = P.V on f16 MFMA; MXFP8 mode adds the bf16 reference row (TV, argmax)
+//      and the per-32-key E4M3/E8M0 probability path.
+//
+// Definitions ("Catnip Week 10 KV Cache Attention Study"): the Structural / Effective / Numerical
+// MXFP8 statistics of the experiment-design section, region masses of the KV-cache banner, frame
+// masses of Figure 2, TV and argmax agreement of the quantization section. Recall@32 and the GQA
+// layout: the MiniCPM5-2B predictor study, section 0. Int4 K/V source: "KV residual window".
+#include "kvprof_internal.h"
+#include "kvprof_device.h"
+
+namespace kvp {
+namespace {
+
+constexpr int NW = 8;   // waves per workgroup: 2 per SIMD, so each lane may use 256 VGPRs
+constexpr int WGT = NW * 64;
+constexpr int ROWS = 16;
+constexpr int HB = 257;  // padded histogram stride (rows land in different LDS banks)
+constexpr int CAP = 256; // candidate slots per row
+constexpr int NT = 4;    // selected ranks per row
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kPScale = 32768.f;  // P is fed to the f16 MFMA as p * 2^15
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct TState {
+  unsigned long long prefix;  // key >> pos of the group holding the target
+  int pos, width;             // current digit position / width in the 48-bit key
+  int cnt_before;             // elements ranked before the group
+  int cnt_in;                 // elements in the group
+  int target;                 // 0-based rank to locate
+  int resolved;
+  unsigned mass_before;       // fixed-point (2^31 = 1) mass ranked before the group
+  float frac;
+};
+
+struct Sel {
+  unsigned hcnt[ROWS][HB];
+  unsigned hmass[ROWS][HB];
+  float ce[ROWS][CAP];
+  int cj[ROWS][CAP];
+  float sorted_e[ROWS][CAP];
+};
+
+struct Smem {
+  float red_a[NW][ROWS];
+  float red_b[NW][ROWS];
+  float red_e[NW][ROWS];
+  int red_i[NW][ROWS];
+  float segpart[NW][ROWS][kSegPerWave];
+  float segmass[ROWS][kMaxSeg];
+  int cs0[NW];
+  float r_z[ROWS], r_inv_fx[ROWS], r_thrz[ROWS], r_m[ROWS], r_e[ROWS];
+  unsigned r_bitsmax[ROWS];
+  int r_sh[ROWS];
+  int flag;
+  TState ts[ROWS][NT];
+  float tmass[ROWS][3];
+  int ncand[ROWS], nwin[ROWS];
+  float win_e[ROWS][32];
+  int win_j[ROWS][32];
+  int top0[ROWS];
+  u32x4 qs[ROWS][16];  // Q rows as 16-byte chunks (B operand of S^T = K Q^T)
+  union {
+    Sel sel;
+    float ored[NW / 2][ROWS][64];
+  } u;
+};
+
+struct RowInfo {
+  bool ok;
+  long long grow;  // global output row
+  int qi;          // query index inside its head
+  int nvis;        // visible keys
+};
+
+__device__ __forceinline__ RowInfo row_info(const RowStatsParams& p, int b, int hkv, int rb, int r) {
+  RowInfo ri;
+  int rl = rb * ROWS + r;
+  ri.ok = rl < p.rows_per_kv;
+  int hloc = ri.ok ? rl / p.n_q : 0;
+  ri.qi = ri.ok ? rl - hloc * p.n_q : 0;
+  int hq = hkv * p.group + hloc;
+  ri.grow = ((long long)b * p.n_heads_q + hq) * p.n_q + ri.qi;
+  int nv = p.n_k;
+  if (p.causal) {
+    long long v = p.q_pos0 + ri.qi + 1;
+    nv = v < (long long)p.n_k ? (int)v : p.n_k;
+  }
+  ri.nvis = ri.ok ? nv : 0;
+  return ri;
+}
+
+// Sum over the 4 lanes that hold one row (lanes r, r+16, r+32, r+48); same result on all four.
+__device__ __forceinline__ float row_sum4(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+__device__ __forceinline__ float row_max4(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float row_min4(float x) {
+  x = fminf(x, __shfl_xor(x, 16));
+  return fminf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ int row_isum4(int x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+// Fixed-order sum over a whole wave.
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Returns x through an empty asm statement: values derived from the copy are computed where the copy
+// is made. Used at the top of each pass over the score registers so that the compiler does not hoist
+// per-key work (validity tests, order keys) out of the pass loops and keep it live in registers.
+template <typename T>
+__device__ __forceinline__ T opaque(T x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// 32-bit order key of e' inside a row: 0 for the largest, dmax for the smallest. Clamped so that every
+// digit extraction sees the same value even if exp2 were not monotone at the last bit.
+__device__ __forceinline__ unsigned dkey(float e, unsigned bitsmax, unsigned dmax) {
+  return min((unsigned)max((int)(bitsmax - __float_as_uint(e)), 0), dmax);
+}
+
+__device__ __forceinline__ int remap_block(int bid, int n) {
+  // Dispatch places consecutive workgroups on the 8 XCDs round-robin; this mapping gives each XCD a
+  // contiguous range of logical blocks, so the row blocks of one KV head share that XCD's L2.
+  if ((n & 7) == 0) {
+    const int per = n >> 3;
+    return (bid & 7) * per + (bid >> 3);
+  }
+  return bid;
+}
+
+// ---- K / Q / V operand loaders ------------------------------------------------------------------
+
+__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8_bits(u32x4 v) {
+  f16x8 h;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    h[2 * c] = (_Float16)__uint_as_float(v[c] << 16);
+    h[2 * c + 1] = (_Float16)__uint_as_float(v[c] & 0xFFFF0000u);
+  }
+  return __builtin_bit_cast(u32x4, h);
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// A byte offset past the end of every buffer this kernel reads (each is far below 1 GiB) that stays
+// clear of 32-bit wrap-around when small constants are added to it.
+constexpr unsigned kOOR = 0x7FFF0000u;
+
+// Buffer resource over [base, base + bytes): loads take one 32-bit offset register, and loads past
+// the end return zero (the hardware range check), which pads ragged key tails.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const size_t cap = 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(bytes < cap ? bytes : cap),
+                                           0x00020000);
+}
+
+// A-operand fragment of K for one 32-wide k-step: key ja, dims d0..d0+7 (d0 = ks*32 + 8g).
+// Int4 blobs: both the 4-bit and the float32-window paths are loaded and one is selected, so there
+// is no divergent branch; offsets outside a section fall outside the buffer and read zeros.
+template <int KSRC>
+__device__ __forceinline__ u32x4 load_k(const RowStatsParams& p, rsrc_t rk, const Int4Layout& L, int ja, int d0) {
+  if (KSRC == KSRC_BF16) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rk, (unsigned)(ja * KVPROF_HEAD_DIM + d0) * 2u, 0, 0);
+  } else {
+    const bool quant = ja < (int)L.n;
+    const int jq = quant ? ja : 0;
+    const uint32_t codes = __builtin_amdgcn_raw_buffer_load_b32(rk, (unsigned)(L.kc + (size_t)jq * 64 + d0 / 2), 0, 0);
+    const unsigned mo = (unsigned)(L.km + ((size_t)(jq >> 5) * 128 + d0) * 4);
+    const u32x4 m0 = __builtin_amdgcn_raw_buffer_load_b128(rk, mo, 0, 0);
+    const u32x4 m1 = __builtin_amdgcn_raw_buffer_load_b128(rk, mo + 16u, 0, 0);
+    // rows of the float32 window; keys before it (or past n_k) read past the buffer end -> zeros
+    const unsigned ro = (quant || ja >= p.n_k) ? kOOR
+                                               : (unsigned)(L.kr + ((size_t)(ja - (int)L.n) * 128 + d0) * 4);
+    const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ro, 0, 0));
+    const f32x4 bb = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ro + 16u, 0, 0));
+    f16x8 h;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t wd = c < 4 ? m0[c] : m1[c - 4];
+      const float sc_ = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xFFFF));
+      const float mn_ = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
+      const float qv = fmaf((float)((codes >> (4 * c)) & 0xF), sc_, mn_);
+      const float rv = c < 4 ? a[c] : bb[c - 4];
+      h[c] = (_Float16)(quant ? qv : rv);
+    }
+    return __builtin_bit_cast(u32x4, h);
+  }
+}
+
+// V value (key j, dim c) as f16 for the P.V product (branchless for int4, as above).
+template <int KSRC>
+__device__ __forceinline__ _Float16 load_v(const RowStatsParams& p, rsrc_t rv, const Int4Layout& L, int j, int c) {
+  if (KSRC == KSRC_BF16) {
+    const uint32_t b = __builtin_amdgcn_raw_buffer_load_b16(rv, (unsigned)(j * KVPROF_HEAD_DIM + c) * 2u, 0, 0);
+    return (_Float16)__uint_as_float(b << 16);
+  } else {
+    const bool quant = j < (int)L.n;
+    const int jq = quant ? j : 0;
+    const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(rv, (unsigned)(L.vc + (size_t)jq * 64 + c / 2), 0, 0);
+    const uint32_t wd = __builtin_amdgcn_raw_buffer_load_b32(rv, (unsigned)(L.vm + ((size_t)jq * 4 + c / 32) * 4), 0, 0);
+    const unsigned ro = (quant || j >= p.n_k) ? kOOR : (unsigned)(L.vr + ((size_t)(j - (int)L.n) * 128 + c) * 4);
+    const uint32_t f = __builtin_amdgcn_raw_buffer_load_b32(rv, ro, 0, 0);
+    const uint32_t code = (byte >> ((c & 1) * 4)) & 0xF;
+    const float s_ = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xFFFF));
+    const float m_ = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
+    return (_Float16)(quant ? fmaf((float)code, s_, m_) : __uint_as_float(f));
+  }
+}
+
+template <int KSRC>
+__device__ __forceinline__ f32x4 mfma_step(u32x4 a, u32x4 b, f32x4 acc) {
+  if (KSRC == KSRC_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+
+// Per-row scan of the 256-bin histogram by one wave (lane holds bins 4*lane..4*lane+3). Locates,
+// for every unresolved target of the row, the bin that holds its rank and narrows the target state.
+__device__ void scan_row(Smem& sm, int row, int lane, int level) {
+  unsigned c[4], m[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    c[q] = sm.u.sel.hcnt[row][4 * lane + q];
+    m[q] = sm.u.sel.hmass[row][4 * lane + q];
+  }
+  unsigned lc = c[0] + c[1] + c[2] + c[3];
+  unsigned lm = m[0] + m[1] + m[2] + m[3];
+  unsigned ic = lc, im = lm;
+  for (int o = 1; o < 64; o <<= 1) {
+    unsigned tc = __shfl_up(ic, o), tm = __shfl_up(im, o);
+    if (lane >= o) {
+      ic += tc;
+      im += tm;
+    }
+  }
+  unsigned run = ic - lc, mrun = im - lm;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    TState& ts = sm.ts[row][t];
+    if (ts.resolved && level > 0) continue;
+    if (level > 0 && ts.width == 0) continue;
+    unsigned T = (unsigned)(ts.target - ts.cnt_before);
+    unsigned r0 = run, m0 = mrun;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (r0 <= T && T < r0 + c[q]) {
+        ts.prefix = (ts.prefix << ts.width) | (unsigned long long)(4 * lane + q);
+        ts.cnt_before += (int)r0;
+        ts.mass_before += m0;
+        ts.cnt_in = (int)c[q];
+        ts.resolved = c[q] <= (unsigned)CAP;
+      }
+      r0 += c[q];
+      m0 += m[q];
+    }
+  }
+}
+
+template <int TPW, int KSRC, bool MX>
+__global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int r = lane & 15;  // query row inside the workgroup
+  const int g = lane >> 4;  // key quad inside a 16-key tile
+
+  const int nrb = (p.rows_per_kv + ROWS - 1) / ROWS;
+  const int nwg = p.n_batch * p.n_heads_kv * nrb;  // < 2^31 (checked on the host)
+  const int bid = remap_block((int)blockIdx.x, nwg);
+  const int rb = bid % nrb;
+  const int hkv = (bid / nrb) % p.n_heads_kv;
+  const int b = bid / (nrb * p.n_heads_kv);
+
+  const RowInfo me = row_info(p, b, hkv, rb, r);
+  const int nvis = me.nvis;
+  // workgroup-uniform extent of visible keys
+  int kmax = nvis;
+  for (int o = 1; o < 16; o <<= 1) kmax = max(kmax, __shfl_xor(kmax, o));
+  kmax = __builtin_amdgcn_readfirstlane(kmax);  // identical on every lane: keep it scalar
+
+  const size_t kvh = (size_t)b * p.n_heads_kv + hkv;
+  const size_t head_bytes = (size_t)p.n_k * KVPROF_HEAD_DIM * 2;
+  rsrc_t rk, rv;
+  if (KSRC == KSRC_BF16) {
+    rk = make_rsrc(p.k + kvh * p.n_k * KVPROF_HEAD_DIM, head_bytes);
+    rv = make_rsrc(p.v ? p.v + kvh * p.n_k * KVPROF_HEAD_DIM : p.k, p.v ? head_bytes : 0);
+  } else {
+    rk = make_rsrc(p.kv_packed + kvh * p.blob_bytes, p.blob_bytes);
+    rv = rk;
+  }
+  const rsrc_t rbias = make_rsrc(p.key_bias ? (const void*)p.key_bias : (const void*)p.q,
+                                 p.key_bias ? (size_t)p.n_k * 4 : 0);
+  Int4Layout L{};
+  if (KSRC == KSRC_INT4) L = int4_layout(p.n_k, KVPROF_HEAD_DIM, p.r_window);
+
+  // clear the shared accumulators
+  for (int i = tid; i < NW * ROWS * kSegPerWave; i += WGT) (&sm.segpart[0][0][0])[i] = 0.f;
+  for (int i = tid; i < ROWS * HB * 2; i += WGT) (&sm.u.sel.hcnt[0][0])[i] = 0u;
+
+  // Q rows of the workgroup into LDS (wave 0): chunk c of row r holds dims 8c .. 8c+7
+  if (w == 0) {
+#pragma unroll
+    for (int c = g; c < 16; c += 4) {
+      u32x4 v = zero4();
+      if (me.ok) {
+        v = *reinterpret_cast<const u32x4*>(p.q + (size_t)me.grow * KVPROF_HEAD_DIM + 8 * c);
+        if (KSRC == KSRC_INT4) v = bf16x8_to_f16x8_bits(v);
+      }
+      sm.qs[r][c] = v;
+    }
+  }
+  __syncthreads();
+
+  // ---- A: scores ---------------------------------------------------------------------------------
+  const int kbase = w * TPW * 16;
+  float sc[TPW][4];
+  float umax = -INFINITY, umin = INFINITY;
+  // The scheduling barrier at the end of each tile keeps the compiler from hoisting every tile's
+  // loads, which would push the score registers out to scratch.
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int j0 = kbase + t * 16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (j0 < kmax) {
+      u32x4 kf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[ks] = load_k<KSRC>(p, rk, L, j0 + r, ks * 32 + 8 * g);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma_step<KSRC>(kf[ks], sm.qs[r][ks * 4 + g], acc);
+    }
+    float bias[4] = {0.f, 0.f, 0.f, 0.f};
+    if (p.key_bias && j0 < kmax) {
+      const int jb = j0 + 4 * g;
+      if (jb + 3 < p.n_k) {
+        f32x4 bv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rbias, (unsigned)jb * 4u, 0, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bias[i] = bv[i] * kLog2e;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bias[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbias, (unsigned)(jb + i) * 4u, 0, 0)) * kLog2e;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + 4 * g + i;
+      float u = fmaf(acc[i], p.scale_log2, bias[i]);
+      const bool valid = j < nvis;
+      u = valid ? u : -INFINITY;
+      // pinned here: otherwise the compiler sinks this epilogue to the next use and keeps both the
+      // MFMA accumulators and the bias values live for every tile
+      sc[t][i] = opaque(u);
+      umax = fmaxf(umax, u);
+      umin = valid ? fminf(umin, u) : umin;
+    }
+    umax = opaque(umax);
+    umin = opaque(umin);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  umax = row_max4(umax);
+  umin = row_min4(umin);
+  if (g == 0) {
+    sm.red_a[w][r] = umax;
+    sm.red_b[w][r] = umin;
+  }
+  // first segment overlapping this wave's keys
+  int cs = 0;
+  while (cs < p.n_seg && p.seg_bounds[cs + 1] <= kbase) ++cs;
+  const int cs_first = cs;
+  if (lane == 0) sm.cs0[w] = cs_first;
+  __syncthreads();
+  float m = -INFINITY, mn = INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    m = fmaxf(m, sm.red_a[ww][r]);
+    mn = fminf(mn, sm.red_b[ww][r]);
+  }
+  if (!me.ok) {
+    m = 0.f;
+    mn = 0.f;
+  }
+
+  // ---- B: exponentials, entropy sum, segment masses -----------------------------------------------
+  const float off = 64.f - m;
+  float esum = 0.f, acc_seg = 0.f;
+  int nb = (cs < p.n_seg) ? p.seg_bounds[cs + 1] : 0x7fffffff;
+  const int gB = opaque(g);
+  auto flush = [&](float a, int seg) {
+    float v = row_sum4(a);
+    if (g == 0 && seg - cs_first < kSegPerWave) sm.segpart[w][r][seg - cs_first] = v;
+  };
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int j0 = kbase + t * 16;
+    if (j0 < kmax) {
+    float e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float tp = fmaxf(sc[t][i] + off, -256.f);
+      e[i] = __builtin_amdgcn_exp2f(tp);
+      esum = fmaf(e[i], tp, esum);
+      sc[t][i] = opaque(e[i]);
+    }
+    if (j0 + 16 <= nb) {
+      acc_seg += (e[0] + e[1]) + (e[2] + e[3]);
+    } else {
+      int lo = j0;
+      while (lo < j0 + 16) {
+        const int hi = min(nb, j0 + 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + 4 * gB + i;
+          if (j >= lo && j < hi) acc_seg += e[i];
+        }
+        lo = hi;
+        if (hi == nb) {
+          flush(acc_seg, cs);
+          acc_seg = 0.f;
+          ++cs;
+          nb = (cs < p.n_seg) ? p.seg_bounds[cs + 1] : 0x7fffffff;
+        }
+      }
+    }
+    }
+    // running sums pinned per tile (else their add chains are sunk past the loop)
+    esum = opaque(esum);
+    acc_seg = opaque(acc_seg);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (kbase < kmax && cs < p.n_seg) flush(acc_seg, cs);
+  esum = row_sum4(esum);
+  if (g == 0) sm.red_e[w][r] = esum;
+  __syncthreads();
+
+  // ---- per-row finalisation of B (wave w handles rows w and w + 8) --------------------------------------------
+  for (int row = w; row < ROWS; row += NW) {
+    const RowInfo ri = row_info(p, b, hkv, rb, row);
+    const int span = TPW * 16;
+    for (int s = lane; s < p.n_seg; s += 64) {
+      float v = 0.f;
+      const int s0 = p.seg_bounds[s], s1 = p.seg_bounds[s + 1];
+      for (int ww = 0; ww < NW; ++ww) {
+        const int w0 = ww * span, w1 = w0 + span;
+        if (w0 < s1 && w1 > s0) {
+          const int slot = s - sm.cs0[ww];
+          if (slot >= 0 && slot < kSegPerWave) v += sm.segpart[ww][row][slot];
+        }
+      }
+      sm.segmass[row][s] = v;
+    }
+    __syncthreads();  // (uniform: every wave runs this block)
+    if (lane == 0) {
+      float z = 0.f;
+      for (int s = 0; s < p.n_seg; ++s) z += sm.segmass[row][s];
+      float e_ = 0.f;
+      for (int ww = 0; ww < NW; ++ww) e_ += sm.red_e[ww][row];
+      if (!ri.ok || !(z > 0.f)) z = 1.f;
+      sm.r_z[row] = z;
+      sm.r_e[row] = e_;
+    }
+  }
+  __syncthreads();
+  const float Zp = sm.r_z[r];
+  const float invZ = 1.f / Zp;
+  // row constants for the selection (every lane of the row computes the same values)
+  const unsigned bitsmax = __float_as_uint(__builtin_amdgcn_exp2f(fmaxf(m + off, -256.f)));
+  const unsigned bitsmin = __float_as_uint(__builtin_amdgcn_exp2f(fmaxf(mn + off, -256.f)));
+  const unsigned dmax = bitsmax - min(bitsmin, bitsmax);
+  const int sh = dmax < 256u ? 0 : (32 - __builtin_clz(dmax)) - 8;
+  const float inv_fx = 2147483648.f / Zp;
+  // 32-bit order key of e' inside the row: 0 for the largest, dmax for the smallest (clamped so that
+  // every later digit extraction sees the same value)
+
+  const float thrz = ldexpf(Zp, -150);
+
+  // region / frame / scalar outputs and target setup (wave w handles rows w and w + 8)
+  for (int row = w; row < ROWS; row += NW) {
+    const RowInfo ri = row_info(p, b, hkv, rb, row);
+    if (ri.ok) {
+      const float z = sm.r_z[row];
+      const float iz = 1.f / z;
+      if (lane < p.n_regions) {
+        float a = 0.f;
+        for (int s = 0; s < p.n_seg; ++s)
+          if (p.seg_region[s] == lane) a += sm.segmass[row][s];
+        if (p.region_mass) p.region_mass[ri.grow * p.n_regions + lane] = a * iz;
+      }
+      for (int f = lane; f < p.n_frames; f += 64) {
+        float a = 0.f;
+        for (int s = 0; s < p.n_seg; ++s)
+          if (p.seg_frame[s] == f) a += sm.segmass[row][s];
+        if (p.frame_mass) p.frame_mass[ri.grow * p.n_frames + f] = a * iz;
+      }
+      if (lane < NT) {
+        const int n = ri.nvis;
+        TState ts;
+        ts.prefix = 0;
+        ts.pos = 16 + 0;  // replaced below by the row's level-1 position
+        ts.width = 8;
+        ts.cnt_before = 0;
+        ts.cnt_in = 0;
+        ts.resolved = 0;
+        ts.mass_before = 0;
+        if (lane == 0) {
+          ts.target = min(31, n - 1);
+          ts.frac = 0.f;
+        } else {
+          const int pct = lane == 1 ? 1 : (lane == 2 ? 5 : 10);
+          ts.target = (n * pct) / 100;
+          ts.frac = (float)((n * pct) % 100) / 100.f;
+        }
+        sm.ts[row][lane] = ts;
+      }
+    } else if (lane < NT) {
+      TState ts{};
+      ts.resolved = 1;
+      ts.width = 0;
+      sm.ts[row][lane] = ts;
+    }
+  }
+
+  // ---- C: level-1 histogram -------------------------------------------------------------------------
+  {
+  const int gq = opaque(g), nv = opaque(nvis);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int j0 = kbase + t * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + 4 * gq + i;
+      if (j < nv) {
+        const float e = sc[t][i];
+        const int dig = (int)(dkey(e, bitsmax, dmax) >> sh);
+        atomicAdd(&sm.u.sel.hcnt[r][dig], 1u);
+        atomicAdd(&sm.u.sel.hmass[r][dig], (unsigned)__builtin_rintf(e * inv_fx));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  }
+  __syncthreads();
+  for (int row = w; row < ROWS; row += NW) {
+    const int shr = __shfl(sh, row);  // lane `row` holds that row's constants
+    if (lane < NT) sm.ts[row][lane].pos = 16 + shr;
+  }
+  __syncthreads();
+  for (int row = w; row < ROWS; row += NW) scan_row(sm, row, lane, 0);
+  __syncthreads();
+
+  // ---- D: refine and gather, one target at a time --------------------------------------------------
+#pragma unroll 1
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll 1
+    for (int level = 1; level <= 8; ++level) {
+      if (tid == 0) sm.flag = 0;
+      __syncthreads();
+      for (int row = w; row < ROWS; row += NW)
+        if (lane == 0 && !sm.ts[row][t].resolved && sm.ts[row][t].width > 0) atomicOr(&sm.flag, 1);
+      __syncthreads();
+      if (!sm.flag) break;
+      // next digit of the 48-bit key (D << 16 | j)
+      const TState tsr = sm.ts[r][t];
+      const bool active_row = !tsr.resolved && tsr.width > 0;
+      int npos = tsr.pos - 8, nwid = 8;
+      if (npos < 0) {
+        nwid = tsr.pos;
+        npos = 0;
+      }
+      for (int i = tid; i < ROWS * HB * 2; i += WGT) (&sm.u.sel.hcnt[0][0])[i] = 0u;
+      __syncthreads();
+      if (active_row) {
+        const int gq = opaque(g), nv = opaque(nvis);
+        const unsigned bmx = opaque(bitsmax), dmx = opaque(dmax);
+        const float ifx = opaque(inv_fx);  // keeps the per-key masses from being hoisted out of the level loop
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+          const int j0 = kbase + tt * 16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = j0 + 4 * gq + i;
+            if (j < nv) {
+              const float e = sc[tt][i];
+              const unsigned D = dkey(e, bmx, dmx);
+              const unsigned long long key = ((unsigned long long)D << 16) | (unsigned)j;
+              if ((key >> (npos + nwid)) == tsr.prefix) {
+                const int dig = (int)((key >> npos) & ((1ull << nwid) - 1));
+                atomicAdd(&sm.u.sel.hcnt[r][dig], 1u);
+                atomicAdd(&sm.u.sel.hmass[r][dig], (unsigned)__builtin_rintf(e * ifx));
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __syncthreads();
+      for (int row = w; row < ROWS; row += NW) {
+        const TState ts = sm.ts[row][t];
+        const bool act = !ts.resolved && ts.width > 0;
+        int wpos = ts.pos - 8, wwid = 8;
+        if (wpos < 0) {
+          wwid = ts.pos;
+          wpos = 0;
+        }
+        unsigned c[4], mm[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c[q] = sm.u.sel.hcnt[row][4 * lane + q];
+          mm[q] = sm.u.sel.hmass[row][4 * lane + q];
+        }
+        unsigned lc = c[0] + c[1] + c[2] + c[3], lm = mm[0] + mm[1] + mm[2] + mm[3];
+        unsigned ic = lc, im = lm;
+        for (int o = 1; o < 64; o <<= 1) {
+          unsigned tc = __shfl_up(ic, o), tm = __shfl_up(im, o);
+          if (lane >= o) {
+            ic += tc;
+            im += tm;
+          }
+        }
+        unsigned r0 = ic - lc, m0 = im - lm;
+        const unsigned T = (unsigned)(ts.target - ts.cnt_before);
+        TState nt = ts;
+        bool found = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (r0 <= T && T < r0 + c[q]) {
+            found = true;
+            nt.prefix = (ts.prefix << wwid) | (unsigned long long)(4 * lane + q);
+            nt.cnt_before = ts.cnt_before + (int)r0;
+            nt.mass_before = ts.mass_before + m0;
+            nt.cnt_in = (int)c[q];
+            nt.pos = wpos;
+            nt.width = wwid;
+            nt.resolved = c[q] <= (unsigned)CAP || wpos == 0;
+          }
+          r0 += c[q];
+          m0 += mm[q];
+        }
+        __syncthreads();
+        if (act && found) sm.ts[row][t] = nt;
+      }
+      __syncthreads();
+    }
+
+    // gather the candidates of target t (and, for the top-32 boundary, every key ranked before it)
+    if (tid < ROWS) {
+      sm.ncand[tid] = 0;
+      if (t == 0) sm.nwin[tid] = 0;
+    }
+    __syncthreads();
+    {
+      const TState tsr = sm.ts[r][t];
+      const bool rowok = me.ok && tsr.width > 0;
+      if (rowok) {
+        const int gq = opaque(g), nv = opaque(nvis);
+        const unsigned bmx = opaque(bitsmax), dmx = opaque(dmax);
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+          const int j0 = kbase + tt * 16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = j0 + 4 * gq + i;
+            if (j < nv) {
+              const float e = sc[tt][i];
+              const unsigned D = dkey(e, bmx, dmx);
+              const unsigned long long key = ((unsigned long long)D << 16) | (unsigned)j;
+              const unsigned long long kp = key >> tsr.pos;
+              if (kp == tsr.prefix) {
+                const int slot = atomicAdd(&sm.ncand[r], 1);
+                if (slot < CAP) {
+                  sm.u.sel.ce[r][slot] = e;
+                  sm.u.sel.cj[r][slot] = j;
+                }
+              } else if (t == 0 && kp < tsr.prefix) {
+                const int slot = atomicAdd(&sm.nwin[r], 1);
+                if (slot < 32) {
+                  sm.win_e[r][slot] = e;
+                  sm.win_j[r][slot] = j;
+                }
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    __syncthreads();
+    // rank the candidates of row w exactly by (e' descending, index ascending)
+    for (int row = w; row < ROWS; row += NW) {
+      const TState ts = sm.ts[row][t];
+      const int c = min(sm.ncand[row], CAP);
+      const unsigned bmx = __shfl(bitsmax, row);
+      if (ts.width > 0) {
+        for (int a = lane; a < c; a += 64) {
+          const float ea = sm.u.sel.ce[row][a];
+          const int ja = sm.u.sel.cj[row][a];
+          const unsigned Da = bmx - __float_as_uint(ea);
+          int rank = 0;
+          for (int q = 0; q < c; ++q) {
+            const unsigned Dq = bmx - __float_as_uint(sm.u.sel.ce[row][q]);
+            const int jq = sm.u.sel.cj[row][q];
+            rank += (Dq < Da) || (Dq == Da && jq < ja);
+          }
+          sm.u.sel.sorted_e[row][rank] = ea;
+          if (t == 0) {
+            const int nsel = ts.target + 1;  // min(32, n)
+            const int slot = ts.cnt_before + rank;
+            if (slot < nsel) {
+              sm.win_e[row][slot] = ea;
+              sm.win_j[row][slot] = ja;
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (t > 0) for (int row = w; row < ROWS; row += NW) {
+      const TState ts = sm.ts[row][t];
+      const RowInfo ri = row_info(p, b, hkv, rb, row);
+      if (ri.ok && ts.width > 0) {
+        const int rr = ts.target - ts.cnt_before;
+        const int c = min(sm.ncand[row], CAP);
+        float a = 0.f;
+        for (int q = lane; q < c; q += 64)
+          if (q < rr) a += sm.u.sel.sorted_e[row][q];
+        a = wave_sum(a);
+        if (lane == 0) {
+          const float iz = 1.f / sm.r_z[row];
+          float mass = (float)ts.mass_before * 0x1p-31f + a * iz;
+          if (rr < c) mass += ts.frac * sm.u.sel.sorted_e[row][rr] * iz;
+          sm.tmass[row][t - 1] = mass;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- E: outputs ---------------------------------------------------------------------------------
+  for (int row = w; row < ROWS; row += NW) {
+    const RowInfo ri = row_info(p, b, hkv, rb, row);
+    const unsigned bmx = __shfl(bitsmax, row);
+    if (ri.ok) {
+      const int nsel = min(32, ri.nvis);
+      int rank = 0, jl = -1;
+      if (lane < nsel) {
+        const float el = sm.win_e[row][lane];
+        jl = sm.win_j[row][lane];
+        const unsigned Dl = bmx - __float_as_uint(el);
+        for (int q = 0; q < nsel; ++q) {
+          const unsigned Dq = bmx - __float_as_uint(sm.win_e[row][q]);
+          const int jq = sm.win_j[row][q];
+          rank += (Dq < Dl) || (Dq == Dl && jq < jl);
+        }
+        if (p.top32) p.top32[ri.grow * 32 + rank] = jl;
+        if (rank == 0) sm.top0[row] = jl;
+      } else if (lane < 32) {
+        if (p.top32) p.top32[ri.grow * 32 + lane] = -1;
+      }
+      if (lane == 0) {
+        const float z = sm.r_z[row];
+        const float e_ = sm.r_e[row];
+        const float H = logf(z) - kLn2 * (e_ / z);
+        if (p.support) p.support[ri.grow] = expf(H) / (float)ri.nvis;
+        if (p.top_mass) {
+          p.top_mass[ri.grow * 3 + 0] = sm.tmass[row][0];
+          p.top_mass[ri.grow * 3 + 1] = sm.tmass[row][1];
+          p.top_mass[ri.grow * 3 + 2] = sm.tmass[row][2];
+        }
+      }
+    }
+  }
+  {
+    // row max / lse: the lane of row r in wave 0 writes them
+    if (w == 0 && g == 0 && me.ok) {
+      if (p.row_max) p.row_max[me.grow] = m * kLn2;
+      if (p.row_lse) p.row_lse[me.grow] = (m + log2f(Zp) - 64.f) * kLn2;
+    }
+  }
+
+  // strict zeros: only rows whose smallest e' can be at or below Z' 2^-150 need a counting pass
+  {
+    const unsigned emin_bits = bitsmin;
+    int need = (me.ok && __uint_as_float(emin_bits) <= thrz) ? 1 : 0;
+    if (tid == 0) sm.flag = 0;
+    __syncthreads();
+    if (need) atomicOr(&sm.flag, 1);
+    __syncthreads();
+    int cnt = 0;
+    if (sm.flag) {
+      const int gq = opaque(g), nv = opaque(nvis);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int j0 = kbase + t * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + 4 * gq + i;
+          cnt += (j < nv && sc[t][i] <= thrz) ? 1 : 0;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    cnt = row_isum4(cnt);
+    if (g == 0) sm.red_i[w][r] = cnt;
+    __syncthreads();
+    if (w == 0 && g == 0 && me.ok) {
+      int tot = 0;
+      for (int ww = 0; ww < NW; ++ww) tot += sm.red_i[ww][r];
+      if (p.strict_zero) p.strict_zero[me.grow] = tot;
+      if (MX && p.argmax) p.argmax[me.grow] = sm.top0[r];
+    }
+  }
+
+  // ---- O = P.V --------------------------------------------------------------------------------------
+  if (p.o) {
+    const float pmul = invZ * kPScale;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      const float pm = opaque(pmul);  // recomputed per half, not hoisted as one f16 pair per tile
+      const int rq = opaque(r), gq = opaque(g);  // likewise the per-key V offsets
+      f32x4 oacc[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int j0 = kbase + t * 16;
+        if (j0 < kmax) {
+        f16x4 pa;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pa[i] = (_Float16)(sc[t][i] * pm);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int c = half * 64 + db * 16 + rq;
+          f16x4 vb;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vb[i] = load_v<KSRC>(p, rv, L, j0 + 4 * gq + i, c);
+          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, oacc[db], 0, 0, 0);
+        }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // fixed-order tree over the 16 waves
+      for (int s = NW / 2; s >= 1; s >>= 1) {
+        if (w >= s && w < 2 * s) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.u.ored[w - s][4 * g + i][db * 16 + r] = oacc[db][i];
+        }
+        __syncthreads();
+        if (w < s) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[db][i] += sm.u.ored[w][4 * g + i][db * 16 + r];
+        }
+        __syncthreads();
+      }
+      if (w == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const RowInfo ri = row_info(p, b, hkv, rb, 4 * g + i);
+          if (ri.ok) {
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+              p.o[ri.grow * KVPROF_HEAD_DIM + half * 64 + db * 16 + r] = oacc[db][i] * (1.f / kPScale);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- MXFP8 mode: bf16 reference row and the probability path ------------------------------------
+  if (MX) {
+    __syncthreads();
+    const rsrc_t rkr = make_rsrc(p.k_ref + kvh * p.n_k * KVPROF_HEAD_DIM, head_bytes);
+    u32x4 qr[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qr[ks] = me.ok ? *reinterpret_cast<const u32x4*>(p.q_ref + (size_t)me.grow * KVPROF_HEAD_DIM + ks * 32 + 8 * g)
+                     : zero4();
+    auto ref_tile = [&](int j0, float (&u)[4]) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int ja = j0 + r;
+        u32x4 kf = __builtin_amdgcn_raw_buffer_load_b128(rkr, (unsigned)(ja * KVPROF_HEAD_DIM + ks * 32 + 8 * g) * 2u, 0, 0);
+        acc = mfma_step<KSRC_BF16>(kf, qr[ks], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + 4 * g + i;
+        float bb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbias, (unsigned)j * 4u, 0, 0)) * kLog2e;
+        u[i] = j < nvis ? fmaf(acc[i], p.scale_log2, bb) : -INFINITY;
+      }
+    };
+    // R1: reference max and argmax (ties to the lowest index)
+    float best = -INFINITY;
+    int bestj = 0x7fffffff;
+#pragma unroll 1
+    for (int t = 0; t < TPW; ++t) {
+      const int j0 = kbase + t * 16;
+      if (j0 >= kmax) break;
+      float u[4];
+      ref_tile(j0, u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + 4 * g + i;
+        if (u[i] > best || (u[i] == best && j < bestj)) {
+          best = u[i];
+          bestj = j;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      float ob = __shfl_xor(best, o);
+      int oj = __shfl_xor(bestj, o);
+      if (ob > best || (ob == best && oj < bestj)) {
+        best = ob;
+        bestj = oj;
+      }
+    }
+    if (g == 0) {
+      sm.red_a[w][r] = best;
+      sm.red_i[w][r] = bestj;
+    }
+    __syncthreads();
+    float mref = -INFINITY;
+    int aref = 0x7fffffff;
+    for (int ww = 0; ww < NW; ++ww) {
+      float ob = sm.red_a[ww][r];
+      int oj = sm.red_i[ww][r];
+      if (ob > mref || (ob == mref && oj < aref)) {
+        mref = ob;
+        aref = oj;
+      }
+    }
+    if (!me.ok) mref = 0.f;
+    __syncthreads();
+    // R2: reference normaliser
+    float zr = 0.f;
+#pragma unroll 1
+    for (int t = 0; t < TPW; ++t) {
+      const int j0 = kbase + t * 16;
+      if (j0 >= kmax) break;
+      float u[4];
+      ref_tile(j0, u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zr += __builtin_amdgcn_exp2f(u[i] - mref);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    zr = row_sum4(zr);
+    if (g == 0) sm.red_b[w][r] = zr;
+    __syncthreads();
+    float Zr = 0.f;
+    for (int ww = 0; ww < NW; ++ww) Zr += sm.red_b[ww][r];
+    const float invZr = me.ok ? 1.f / Zr : 0.f;
+    __syncthreads();
+    // R3: TV between the MX row and the reference row, and the P path
+    float tv = 0.f, pz = 0.f, tvp = 0.f, psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < TPW; t += 2) {
+      const int j0 = kbase + t * 16;
+      if (j0 < kmax) {
+      float pv[2][4];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        float u[4];
+        ref_tile(j0 + 16 * h2, u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pm = sc[t + h2][i] * invZ;
+          pv[h2][i] = pm;
+          tv += fabsf(pm - __builtin_amdgcn_exp2f(u[i] - mref) * invZr);
+        }
+      }
+      // one 32-key block: keys j0 .. j0+31 (tiles t, t+1)
+      float amax = 0.f;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, pv[h2][i]);
+      amax = row_max4(amax);
+      const int eb = e8m0_exp(amax);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + 16 * h2 + 4 * g + i;
+          if (j < nvis) {
+            const float pm = pv[h2][i];
+            const float ph = ldexpf(e4m3_value(e4m3_rne(ldexpf(pm, -eb))), eb);
+            pz += (pm > 0.f && ph == 0.f) ? 1.f : 0.f;
+            tvp += fabsf(ph - pm);
+            psum += ph;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    tv = row_sum4(tv);
+    pz = row_sum4(pz);
+    tvp = row_sum4(tvp);
+    psum = row_sum4(psum);
+    if (g == 0) {
+      sm.red_a[w][r] = tv;
+      sm.red_b[w][r] = tvp;
+      sm.segpart[w][r][0] = pz;
+      sm.segpart[w][r][1] = psum;
+    }
+    __syncthreads();
+    if (w == 0 && g == 0 && me.ok) {
+      float a = 0.f, bq = 0.f, c = 0.f, d = 0.f;
+      for (int ww = 0; ww < NW; ++ww) {
+        a += sm.red_a[ww][r];
+        bq += sm.red_b[ww][r];
+        c += sm.segpart[ww][r][0];
+        d += sm.segpart[ww][r][1];
+      }
+      if (p.tv_qk) p.tv_qk[me.grow] = 0.5f * a;
+      if (p.tv_p) p.tv_p[me.grow] = 0.5f * bq;
+      if (p.p_zero_frac) p.p_zero_frac[me.grow] = c / (float)me.nvis;
+      if (p.p_rowsum) p.p_rowsum[me.grow] = d;
+      if (p.argmax_ref) p.argmax_ref[me.grow] = aref;
+    }
+  }
+}
+
+template <int TPW, int KSRC, bool MX>
+hipError_t launch_t(const RowStatsParams& p, hipStream_t s) {
+  const int nrb = (p.rows_per_kv + ROWS - 1) / ROWS;
+  const long long nwg = (long long)p.n_batch * p.n_heads_kv * nrb;
+  if (nwg == 0) return hipSuccess;
+  hipLaunchKernelGGL((row_kernel<TPW, KSRC, MX>), dim3((unsigned)nwg), dim3(WGT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int row_stats_tpw_for(int n_k, bool mx) {
+  const int need = (n_k + NW * 16 - 1) / (NW * 16);
+  static const int kT[] = {1, 2, 4, 8, 16, 24, 32, 40, 50};
+  static const int kTmx[] = {2, 4, 8, 16};
+  if (mx) {
+    for (int t : kTmx)
+      if (t >= need) return t;
+    return -1;
+  }
+  for (int t : kT)
+    if (t >= need) return t;
+  return -1;
+}
+
+hipError_t launch_row_stats(const RowStatsParams& p, int tpw, int ksrc, bool mx, hipStream_t s) {
+  if (mx) {
+    switch (tpw) {
+      case 2: return launch_t<2, KSRC_BF16, true>(p, s);
+      case 4: return launch_t<4, KSRC_BF16, true>(p, s);
+      case 8: return launch_t<8, KSRC_BF16, true>(p, s);
+      case 16: return launch_t<16, KSRC_BF16, true>(p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (ksrc == KSRC_INT4) {
+    switch (tpw) {
+      case 1: return launch_t<1, KSRC_INT4, false>(p, s);
+      case 2: return launch_t<2, KSRC_INT4, false>(p, s);
+      case 4: return launch_t<4, KSRC_INT4, false>(p, s);
+      case 8: return launch_t<8, KSRC_INT4, false>(p, s);
+      case 16: return launch_t<16, KSRC_INT4, false>(p, s);
+      case 24: return launch_t<24, KSRC_INT4, false>(p, s);
+      case 32: return launch_t<32, KSRC_INT4, false>(p, s);
+      case 40: return launch_t<40, KSRC_INT4, false>(p, s);
+      case 50: return launch_t<50, KSRC_INT4, false>(p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (tpw) {
+    case 1: return launch_t<1, KSRC_BF16, false>(p, s);
+    case 2: return launch_t<2, KSRC_BF16, false>(p, s);
+    case 4: return launch_t<4, KSRC_BF16, false>(p, s);
+    case 8: return launch_t<8, KSRC_BF16, false>(p, s);
+    case 16: return launch_t<16, KSRC_BF16, false>(p, s);
+    case 24: return launch_t<24, KSRC_BF16, false>(p, s);
+    case 32: return launch_t<32, KSRC_BF16, false>(p, s);
+    case 40: return launch_t<40, KSRC_BF16, false>(p, s);
+    case 50: return launch_t<50, KSRC_BF16, false>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvp

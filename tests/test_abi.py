@@ -1,0 +1,118 @@
+"""CPU checks of the C ABI: the library loads, exports every function the header declares, computes
+the host-side payload formula, and rejects invalid arguments before touching a device (every call
+below fails validation, so no GPU is needed)."""
+import ctypes
+import json
+import os
+
+import pytest
+
+from quantized_kv_amd import binding as B
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = B.declared_functions()
+    assert {"kvprof_pack_mxfp8", "kvprof_pack_int4kv", "kvprof_row_stats", "kvprof_attend",
+            "kvprof_int4kv_bytes", "kvprof_compare", "kvprof_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.kvprof_abi_version() == 1
+
+
+def test_args_struct_layout_matches_header():
+    # offsets fixed by the C layout rules on x86-64 / LP64
+    assert B.KvprofArgs.scale.offset == 28
+    assert B.KvprofArgs.q.offset == 32
+    assert B.KvprofArgs.workspace_bytes.offset + 8 == ctypes.sizeof(B.KvprofArgs)
+
+
+def test_payload_pins_through_the_library(lib):
+    g = json.load(open(os.path.join(GOLDEN, "p2_payload.json")))
+    for row in g["rows"]:
+        assert B.kvprof_int4kv_bytes(g["n_tokens"], 32, row["r_window"]) == row["payload_bytes"]
+    # decode shape: N = 4096, d = 128
+    assert [B.kvprof_int4kv_bytes(4096, 128, r) for r in (0, 16, 64)] == [655376, 670480, 710672]
+    assert B.kvprof_int4kv_bytes(10, 32, 11) == 0  # R > N
+    assert B.kvprof_int4kv_bytes(10, 33, 0) == 0  # d not a multiple of 32
+
+
+def _err(lib):
+    return lib.kvprof_last_error().decode()
+
+
+def test_codec_validation(lib):
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.kvprof_pack_mxfp8(fake, 4, 48, None, fake, fake, None) == B.KVPROF_ESHAPE
+    assert "multiple of 32" in _err(lib)
+    assert lib.kvprof_pack_mxfp8(fake, 4, 96, fake, fake, fake, None) == B.KVPROF_ESHAPE  # rotate, not 2^k
+    assert lib.kvprof_pack_mxfp8(None, 4, 128, None, fake, fake, None) == B.KVPROF_EINVAL
+    assert lib.kvprof_pack_mxfp8(fake, -1, 128, None, fake, fake, None) == B.KVPROF_EINVAL
+    assert lib.kvprof_pack_int4kv(fake, fake, 2, 128, 32, 129, fake, 1 << 20, None) == B.KVPROF_EINVAL
+    assert lib.kvprof_pack_int4kv(fake, fake, 2, 128, 32, 16, fake, 100, None) == B.KVPROF_ESIZE
+    assert lib.kvprof_pack_int4kv(fake, fake, 2, 128, 32, 16, ctypes.c_void_p(0x1001), 1 << 20, None) == B.KVPROF_EALIGN
+    assert lib.kvprof_pack_int4kv(fake, fake, 2, 128, 40, 16, fake, 1 << 20, None) == B.KVPROF_ESHAPE
+
+
+def _args(**over):
+    a = B.KvprofArgs()
+    a.mode = B.MODE_BF16
+    a.n_batch, a.n_heads_q, a.n_heads_kv, a.n_q, a.n_k, a.d = 1, 4, 2, 16, 256, 128
+    a.scale = 0.088
+    a.q = a.k = a.v = 0x10000
+    a.support = 0x20000
+    for k_, v_ in over.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("over,code,needle", [
+    (dict(d=64), B.KVPROF_ESHAPE, "head dimension"),
+    (dict(n_heads_q=3), B.KVPROF_ESHAPE, "multiple of n_heads_kv"),
+    (dict(n_k=7000), B.KVPROF_EUNSUPPORTED, "exceeds"),
+    (dict(n_k=0), B.KVPROF_ESHAPE, "n_k"),
+    (dict(q=0), B.KVPROF_EINVAL, "q is null"),
+    (dict(q=0x10008), B.KVPROF_EALIGN, "16-byte"),
+    (dict(mode=7), B.KVPROF_EINVAL, "unknown mode"),
+    (dict(mode=B.MODE_MXFP8), B.KVPROF_EINVAL, "q_codes"),
+    (dict(mode=B.MODE_MXFP8, n_k=4096, q_codes=1, q_scales=1, k_codes=1, k_scales=1), B.KVPROF_EUNSUPPORTED, "exceeds"),
+    (dict(mode=B.MODE_INT4KV), B.KVPROF_EINVAL, "kv_packed"),
+    (dict(causal=2), B.KVPROF_EINVAL, "causal"),
+    (dict(q_pos0=-1), B.KVPROF_EINVAL, "q_pos0"),
+    (dict(o=0x30000, v=0), B.KVPROF_EINVAL, "o needs v"),
+    (dict(frame_mass=0x30000), B.KVPROF_EINVAL, "n_frames"),
+    (dict(tv_qk=0x30000), B.KVPROF_EINVAL, "MXFP8"),
+    (dict(n_frames=65, frame_len=10), B.KVPROF_EUNSUPPORTED, "n_frames"),
+    (dict(hist=0x30000), B.KVPROF_EINVAL, "hist_bins"),
+    (dict(support=0x20002), B.KVPROF_EALIGN, "4-byte"),
+])
+def test_row_stats_validation(lib, over, code, needle):
+    a = _args(**over)
+    assert lib.kvprof_row_stats(ctypes.byref(a), None) == code
+    assert needle in _err(lib)
+
+
+def test_region_and_workspace_validation(lib):
+    rb = (ctypes.c_int32 * 3)(0, 300, 256)
+    a = _args(n_regions=2, region_bounds=rb)
+    assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_ESHAPE
+    rb = (ctypes.c_int32 * 3)(0, 200, 100)
+    a = _args(n_regions=2, region_bounds=rb)
+    assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_ESHAPE
+    # too many tiny segments inside one wave's key slice
+    a = _args(n_frames=64, frame_len=2, frame_mass=0x30000)
+    assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_EUNSUPPORTED
+    # MX mode needs a workspace for the decoded Q/K
+    a = _args(mode=B.MODE_MXFP8, q_codes=1, q_scales=1, k_codes=1, k_scales=1)
+    need = lib.kvprof_workspace_bytes(ctypes.byref(a))
+    assert need >= (1 * 4 * 16 + 1 * 2 * 256) * 128 * 2
+    assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_ESIZE
+    a = _args()
+    assert lib.kvprof_attend(ctypes.byref(a), None) == B.KVPROF_EINVAL  # attend needs o
+    assert lib.kvprof_compare(None, None, None, None, 4, 128, None, None, None, None) == B.KVPROF_EINVAL
