@@ -1,0 +1,204 @@
+"""Benchmark of the KV-cache attention row profiler on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload sampled|full_rows|decode] [--no-cpu-baseline]
+
+A step is one kvprof_row_stats call over the whole workload with every statistic the workload
+reports, inputs already resident in HBM:
+
+* sampled   (default): 42 records x 32 heads x 96 sampled queries against 6,240 cached keys (16 key
+             frames x 390 tokens, [sink 4 | recent 6 | current 6] frames), +0.5 current-chunk bias;
+             support, top-1/5/10 % mass, top-32 indices, strict zeros, region and frame masses,
+             row max / lse, the 6x16 per-head temporal heatmaps and per-record histograms.
+* full_rows: the same for 2,340 queries per head (one record per step by default, --records).
+* decode   : 16 query heads sharing 2 KV heads, 4,096 cached keys, last 256 positions, attention
+             output over the packed 4-bit K/V (R = 16) with top-32 and recent-window mass.
+
+Prints one JSON line (metric, value in rows/s, roofline of the row kernel, oracle CPU baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "query-head rows/s at Sk=6240 (full stats) + % of bf16 MFMA / HBM roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode"])
+    ap.add_argument("--records", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def video_inputs(n_records: int, sampled: bool, dev):
+    import torch
+
+    from quantized_kv_amd import inputs
+
+    qs, ks = [], []
+    for r in range(n_records):
+        rec = inputs.video_record(r, with_v=False, sampled=sampled)
+        qs.append(rec.q.to(dev))
+        ks.append(rec.k.to(dev))
+    return torch.stack(qs), torch.stack(ks)
+
+
+def time_it(fn, steps, warmup, stream):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps  # ms per call
+
+
+def cpu_baseline_video(n_heads: int, sampled: bool):
+    """The oracle, as it stands, on record 0 restricted to n_heads heads (one BLAS thread)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kvprof_oracle as O
+    from quantized_kv_amd import inputs
+
+    rec = inputs.video_record(0, heads=n_heads, with_v=False, sampled=sampled)
+    q, k = inputs.bf16_values(rec.q), inputs.bf16_values(rec.k)
+    bias = inputs.video_key_bias().astype(np.float64)
+    with threadpool_limits(1):
+        t = time.perf_counter()
+        rows = 0
+        for h in range(n_heads):
+            O.row_stats(q[h], k[h], scale=128 ** -0.5, key_bias=bias, region_bounds=inputs.VIDEO_REGION_BOUNDS,
+                        frame_len=inputs.LF_TOKENS, n_frames=inputs.N_KEY_FRAMES)
+            rows += q.shape[1]
+        dt = time.perf_counter() - t
+    return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"record 0, {n_heads} heads x {q.shape[1]} queries x 6240 keys ({rows} rows, {dt:.1f} s)"}
+
+
+def run_video(args, sampled: bool):
+    import torch
+
+    from quantized_kv_amd import binding as B
+    from quantized_kv_amd import inputs
+
+    dev = torch.device("cuda:0")
+    n_rec = args.records or (inputs.N_RECORDS if sampled else 1)
+    t_gen = time.time()
+    Q, K = video_inputs(n_rec, sampled, dev)
+    gen_s = time.time() - t_gen
+    Bn, H, Mq, _ = Q.shape
+    Sk = K.shape[2]
+    rows = Bn * H * Mq
+    bias = torch.from_numpy(inputs.video_key_bias()).to(dev)
+    groups = torch.from_numpy(inputs.video_sample_groups() if sampled else
+                              (torch.arange(Mq) // inputs.LF_TOKENS).numpy().astype("int32")).to(dev)
+    kw = dict(scale=128 ** -0.5, key_bias=bias, region_bounds=inputs.VIDEO_REGION_BOUNDS,
+              frame_len=inputs.LF_TOKENS, n_frames=inputs.N_KEY_FRAMES, row_group=groups, n_groups=6)
+    want = ("support", "top_mass", "top32", "strict_zero", "region_mass", "frame_mass", "row_max", "row_lse")
+    stream = torch.cuda.current_stream()
+    # one allocation of outputs + workspace, then repeated calls on the same buffers
+    res = B.run(Q, K, want=want, heatmap=True, hist=True, **kw)
+    args_full = res["_keepalive"][0]
+    # the row kernel alone (frame masses still written; no heatmap / histogram kernels)
+    res_rows = B.run(Q, K, want=want, **kw)
+    args_rows = res_rows["_keepalive"][0]
+    step = lambda: B.kvprof_row_stats(args_full, stream)  # noqa: E731
+    kern = lambda: B.kvprof_row_stats(args_rows, stream)  # noqa: E731
+    ms = time_it(step, args.steps, args.warmup, stream)
+    ms_kernel = time_it(kern, args.steps, 1, stream)
+    # algorithmic bytes per launch: K once per (record, head), Q rows, bias, and every output
+    out_bytes_row = 4 + 12 + 128 + 4 + 12 + 64 + 4 + 4
+    nbytes = K.numel() * 2 + Q.numel() * 2 + Sk * 4 + rows * out_bytes_row
+    flops = 2.0 * 128 * Sk * rows
+    achieved_gbs = nbytes / (ms_kernel * 1e-3) / 1e9
+    achieved_tfs = flops / (ms_kernel * 1e-3) / 1e12
+    if sampled:
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved_tfs, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved_tfs / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    out = {
+        "metric": METRIC, "value": round(rows / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": ("video steady chunk, sampled queries" if sampled else "video steady chunk, full rows"),
+                   "records": Bn, "heads": H, "queries_per_head": Mq, "keys": Sk, "head_dim": 128,
+                   "rows_per_step": rows, "outputs": list(want) + ["heatmap", "hist"]},
+        "roofline": roof,
+        "row_kernel_ms": round(ms_kernel, 4),
+        "input_gen_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_video(2 if sampled else 1, sampled)
+    return out
+
+
+def run_decode(args):
+    import torch
+
+    from quantized_kv_amd import binding as B
+    from quantized_kv_amd import inputs
+
+    dev = torch.device("cuda:0")
+    Q, K, V = inputs.decode_inputs(5)
+    L, Mq, R = inputs.DECODE_L, inputs.DECODE_MQ, 16
+    Qd = Q[None].to(dev)
+    packed = B.kvprof_pack_int4kv(K.to(dev), V.to(dev), R)
+    stream = torch.cuda.current_stream()
+    res = B.run(Qd, None, want=("top32", "o", "region_mass"), attend=True, mode=B.MODE_INT4KV, kv_packed=packed,
+                r_window=R, n_k=L, n_heads_kv=2, causal=True, q_pos0=L - Mq, region_bounds=[0, L - R, L])
+    a = res["_keepalive"][0]
+    ms = time_it(lambda: B.kvprof_attend(a, stream), args.steps, args.warmup, stream)
+    rows = Q.shape[0] * Mq
+    vis = sum(L - Mq + i + 1 for i in range(Mq)) * Q.shape[0]
+    flops = 4.0 * 128 * vis
+    tfs = flops / (ms * 1e-3) / 1e12
+    return {"metric": METRIC, "value": round(rows / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+            "config": {"workload": "decode GQA over 4-bit KV, R=16", "q_heads": 16, "kv_heads": 2, "keys": L,
+                       "positions": Mq},
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tfs / BF16_PEAK_TFLOPS, 5), "traffic": None}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    from quantized_kv_amd import binding as B
+
+    B.load()
+    assert torch.cuda.is_available(), "needs a GPU"
+    if args.workload == "decode":
+        out = run_decode(args)
+    else:
+        out = run_video(args, sampled=args.workload == "sampled")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

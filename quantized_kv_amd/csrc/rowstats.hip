@@ -7,9 +7,11 @@
 // over registers, with cross-lane / cross-wave reductions in a fixed order (bitwise deterministic):
 //
 //   A  scores u = (scale q.k + b) log2(e) on bf16 / f16 MFMA; row max and min
-//   B  e' = 2^(u - max + 64) (offset keeps strict-zero decisions in the normal float range);
-//      Z', sum e'(u - max + 64) for the entropy; per-segment masses (regions and key frames)
-//   C  256-bin histogram of D = bits(e'max) - bits(e') (monotone in e'), counts and fixed-point masses
+//   B  e' = 2^(u - max + 64) (the offset keeps sums and the strict-zero test in the normal float
+//      range); Z', sum e'(u - max + 64) for the entropy; per-segment masses (regions, key frames).
+//      The registers keep u: ranks are taken on scores, which never underflow.
+//   C  256-bin histogram of the order key D = (max - u) scaled to the row's score range, with counts
+//      and fixed-point masses
 //   D  exact selection of four ranks (top-32 boundary, top-1/5/10 %): boundary bins are refined by
 //      further radix levels on the 48-bit key (D, key index) until at most 256 candidates remain,
 //      which are ranked exactly in LDS
@@ -57,7 +59,7 @@ struct TState {
 struct Sel {
   unsigned hcnt[ROWS][HB];
   unsigned hmass[ROWS][HB];
-  float ce[ROWS][CAP];
+  float ce[ROWS][CAP];  // candidate scores u
   int cj[ROWS][CAP];
   float sorted_e[ROWS][CAP];
 };
@@ -70,14 +72,12 @@ struct Smem {
   float segpart[NW][ROWS][kSegPerWave];
   float segmass[ROWS][kMaxSeg];
   int cs0[NW];
-  float r_z[ROWS], r_inv_fx[ROWS], r_thrz[ROWS], r_m[ROWS], r_e[ROWS];
-  unsigned r_bitsmax[ROWS];
-  int r_sh[ROWS];
+  float r_z[ROWS], r_e[ROWS];
   int flag;
   TState ts[ROWS][NT];
   float tmass[ROWS][3];
   int ncand[ROWS], nwin[ROWS];
-  float win_e[ROWS][32];
+  float win_u[ROWS][32];  // scores of the top-32 keys
   int win_j[ROWS][32];
   int top0[ROWS];
   u32x4 qs[ROWS][16];  // Q rows as 16-byte chunks (B operand of S^T = K Q^T)
@@ -145,11 +145,13 @@ __device__ __forceinline__ T opaque(T x) {
   return x;
 }
 
-// 32-bit order key of e' inside a row: 0 for the largest, dmax for the smallest. Clamped so that every
-// digit extraction sees the same value even if exp2 were not monotone at the last bit.
-__device__ __forceinline__ unsigned dkey(float e, unsigned bitsmax, unsigned dmax) {
-  return min((unsigned)max((int)(bitsmax - __float_as_uint(e)), 0), dmax);
+// 32-bit order key of a score u inside its row: (max - u) scaled so that the row's range [min, max]
+// spans [0, 2^32). Monotone (a larger score never gets a larger key) and free of underflow, unlike
+// probabilities; explicit rounding intrinsics make every pass compute the identical key.
+__device__ __forceinline__ unsigned dkey(float u, float m, float kscale) {
+  return (unsigned)fminf(__fmul_rn(__fsub_rn(m, u), kscale), 4294967040.f);
 }
+constexpr int kSh = 24;  // level-1 digit = key >> 24 (256 equal bins over the row's score range)
 
 __device__ __forceinline__ int remap_block(int bid, int n) {
   // Dispatch places consecutive workgroups on the 8 XCDs round-robin; this mapping gives each XCD a
@@ -192,8 +194,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
 // A-operand fragment of K for one 32-wide k-step: key ja, dims d0..d0+7 (d0 = ks*32 + 8g).
 // Int4 blobs: both the 4-bit and the float32-window paths are loaded and one is selected, so there
 // is no divergent branch; offsets outside a section fall outside the buffer and read zeros.
+// Dequantized int4 K is fed to the f16 MFMA as hi + lo halves (hi = f16(x), lo = f16(x - hi)): 22
+// significant bits, so the scores carry only the float32 accumulation error, like the bf16 path.
 template <int KSRC>
-__device__ __forceinline__ u32x4 load_k(const RowStatsParams& p, rsrc_t rk, const Int4Layout& L, int ja, int d0) {
+__device__ __forceinline__ u32x4 load_k(const RowStatsParams& p, rsrc_t rk, const Int4Layout& L, int ja, int d0,
+                                        u32x4* lo_out = nullptr) {
   if (KSRC == KSRC_BF16) {
     return __builtin_amdgcn_raw_buffer_load_b128(rk, (unsigned)(ja * KVPROF_HEAD_DIM + d0) * 2u, 0, 0);
   } else {
@@ -208,7 +213,7 @@ __device__ __forceinline__ u32x4 load_k(const RowStatsParams& p, rsrc_t rk, cons
                                                : (unsigned)(L.kr + ((size_t)(ja - (int)L.n) * 128 + d0) * 4);
     const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ro, 0, 0));
     const f32x4 bb = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ro + 16u, 0, 0));
-    f16x8 h;
+    f16x8 h, hl;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint32_t wd = c < 4 ? m0[c] : m1[c - 4];
@@ -216,8 +221,11 @@ __device__ __forceinline__ u32x4 load_k(const RowStatsParams& p, rsrc_t rk, cons
       const float mn_ = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
       const float qv = fmaf((float)((codes >> (4 * c)) & 0xF), sc_, mn_);
       const float rv = c < 4 ? a[c] : bb[c - 4];
-      h[c] = (_Float16)(quant ? qv : rv);
+      const float x = quant ? qv : rv;
+      h[c] = (_Float16)x;
+      hl[c] = (_Float16)(x - (float)h[c]);
     }
+    if (lo_out) *lo_out = __builtin_bit_cast(u32x4, hl);
     return __builtin_bit_cast(u32x4, h);
   }
 }
@@ -359,11 +367,14 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     const int j0 = kbase + t * 16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (j0 < kmax) {
-      u32x4 kf[4];
+      u32x4 kf[4], kl[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[ks] = load_k<KSRC>(p, rk, L, j0 + r, ks * 32 + 8 * g);
+      for (int ks = 0; ks < 4; ++ks) kf[ks] = load_k<KSRC>(p, rk, L, j0 + r, ks * 32 + 8 * g, KSRC == KSRC_INT4 ? &kl[ks] : nullptr);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma_step<KSRC>(kf[ks], sm.qs[r][ks * 4 + g], acc);
+      for (int ks = 0; ks < 4; ++ks) {
+        acc = mfma_step<KSRC>(kf[ks], sm.qs[r][ks * 4 + g], acc);
+        if (KSRC == KSRC_INT4) acc = mfma_step<KSRC>(kl[ks], sm.qs[r][ks * 4 + g], acc);
+      }
     }
     float bias[4] = {0.f, 0.f, 0.f, 0.f};
     if (p.key_bias && j0 < kmax) {
@@ -436,7 +447,6 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       float tp = fmaxf(sc[t][i] + off, -256.f);
       e[i] = __builtin_amdgcn_exp2f(tp);
       esum = fmaf(e[i], tp, esum);
-      sc[t][i] = opaque(e[i]);
     }
     if (j0 + 16 <= nb) {
       acc_seg += (e[0] + e[1]) + (e[2] + e[3]);
@@ -500,15 +510,11 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   const float Zp = sm.r_z[r];
   const float invZ = 1.f / Zp;
   // row constants for the selection (every lane of the row computes the same values)
-  const unsigned bitsmax = __float_as_uint(__builtin_amdgcn_exp2f(fmaxf(m + off, -256.f)));
-  const unsigned bitsmin = __float_as_uint(__builtin_amdgcn_exp2f(fmaxf(mn + off, -256.f)));
-  const unsigned dmax = bitsmax - min(bitsmin, bitsmax);
-  const int sh = dmax < 256u ? 0 : (32 - __builtin_clz(dmax)) - 8;
+  const float kscale = (m - mn > 0.f) ? 4294967040.f / (m - mn) : 0.f;
   const float inv_fx = 2147483648.f / Zp;
-  // 32-bit order key of e' inside the row: 0 for the largest, dmax for the smallest (clamped so that
-  // every later digit extraction sees the same value)
 
-  const float thrz = ldexpf(Zp, -150);
+  // p <= 2^-150 (an fp32 zero) <=> u - max + 64 - log2 Z' <= -150
+  const float thr_u = m + log2f(Zp) - 214.f;
 
   // region / frame / scalar outputs and target setup (wave w handles rows w and w + 8)
   for (int row = w; row < ROWS; row += NW) {
@@ -532,7 +538,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         const int n = ri.nvis;
         TState ts;
         ts.prefix = 0;
-        ts.pos = 16 + 0;  // replaced below by the row's level-1 position
+        ts.pos = 16 + kSh;
         ts.width = 8;
         ts.cnt_before = 0;
         ts.cnt_in = 0;
@@ -566,19 +572,15 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     for (int i = 0; i < 4; ++i) {
       const int j = j0 + 4 * gq + i;
       if (j < nv) {
-        const float e = sc[t][i];
-        const int dig = (int)(dkey(e, bitsmax, dmax) >> sh);
+        const float u = sc[t][i];
+        const float e = __builtin_amdgcn_exp2f(fmaxf(u + off, -256.f));
+        const int dig = (int)(dkey(u, m, kscale) >> kSh);
         atomicAdd(&sm.u.sel.hcnt[r][dig], 1u);
         atomicAdd(&sm.u.sel.hmass[r][dig], (unsigned)__builtin_rintf(e * inv_fx));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  }
-  __syncthreads();
-  for (int row = w; row < ROWS; row += NW) {
-    const int shr = __shfl(sh, row);  // lane `row` holds that row's constants
-    if (lane < NT) sm.ts[row][lane].pos = 16 + shr;
   }
   __syncthreads();
   for (int row = w; row < ROWS; row += NW) scan_row(sm, row, lane, 0);
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       __syncthreads();
       if (active_row) {
         const int gq = opaque(g), nv = opaque(nvis);
-        const unsigned bmx = opaque(bitsmax), dmx = opaque(dmax);
+        const float mq = opaque(m), ksq = opaque(kscale), offq = opaque(off);
         const float ifx = opaque(inv_fx);  // keeps the per-key masses from being hoisted out of the level loop
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
@@ -616,11 +618,12 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           for (int i = 0; i < 4; ++i) {
             const int j = j0 + 4 * gq + i;
             if (j < nv) {
-              const float e = sc[tt][i];
-              const unsigned D = dkey(e, bmx, dmx);
+              const float u = sc[tt][i];
+              const unsigned D = dkey(u, mq, ksq);
               const unsigned long long key = ((unsigned long long)D << 16) | (unsigned)j;
               if ((key >> (npos + nwid)) == tsr.prefix) {
                 const int dig = (int)((key >> npos) & ((1ull << nwid) - 1));
+                const float e = __builtin_amdgcn_exp2f(fmaxf(u + offq, -256.f));
                 atomicAdd(&sm.u.sel.hcnt[r][dig], 1u);
                 atomicAdd(&sm.u.sel.hmass[r][dig], (unsigned)__builtin_rintf(e * ifx));
               }
@@ -689,7 +692,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       const bool rowok = me.ok && tsr.width > 0;
       if (rowok) {
         const int gq = opaque(g), nv = opaque(nvis);
-        const unsigned bmx = opaque(bitsmax), dmx = opaque(dmax);
+        const float mq = opaque(m), ksq = opaque(kscale);
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const int j0 = kbase + tt * 16;
@@ -697,20 +700,20 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           for (int i = 0; i < 4; ++i) {
             const int j = j0 + 4 * gq + i;
             if (j < nv) {
-              const float e = sc[tt][i];
-              const unsigned D = dkey(e, bmx, dmx);
+              const float u = sc[tt][i];
+              const unsigned D = dkey(u, mq, ksq);
               const unsigned long long key = ((unsigned long long)D << 16) | (unsigned)j;
               const unsigned long long kp = key >> tsr.pos;
               if (kp == tsr.prefix) {
                 const int slot = atomicAdd(&sm.ncand[r], 1);
                 if (slot < CAP) {
-                  sm.u.sel.ce[r][slot] = e;
+                  sm.u.sel.ce[r][slot] = u;
                   sm.u.sel.cj[r][slot] = j;
                 }
               } else if (t == 0 && kp < tsr.prefix) {
                 const int slot = atomicAdd(&sm.nwin[r], 1);
                 if (slot < 32) {
-                  sm.win_e[r][slot] = e;
+                  sm.win_u[r][slot] = u;
                   sm.win_j[r][slot] = j;
                 }
               }
@@ -725,24 +728,24 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     for (int row = w; row < ROWS; row += NW) {
       const TState ts = sm.ts[row][t];
       const int c = min(sm.ncand[row], CAP);
-      const unsigned bmx = __shfl(bitsmax, row);
+      const float mr = __shfl(m, row), ksr = __shfl(kscale, row);  // lane `row` holds that row
       if (ts.width > 0) {
         for (int a = lane; a < c; a += 64) {
-          const float ea = sm.u.sel.ce[row][a];
+          const float ua = sm.u.sel.ce[row][a];
           const int ja = sm.u.sel.cj[row][a];
-          const unsigned Da = bmx - __float_as_uint(ea);
+          const unsigned Da = dkey(ua, mr, ksr);
           int rank = 0;
           for (int q = 0; q < c; ++q) {
-            const unsigned Dq = bmx - __float_as_uint(sm.u.sel.ce[row][q]);
+            const unsigned Dq = dkey(sm.u.sel.ce[row][q], mr, ksr);
             const int jq = sm.u.sel.cj[row][q];
             rank += (Dq < Da) || (Dq == Da && jq < ja);
           }
-          sm.u.sel.sorted_e[row][rank] = ea;
+          sm.u.sel.sorted_e[row][rank] = __builtin_amdgcn_exp2f(fmaxf(ua + (64.f - mr), -256.f));
           if (t == 0) {
             const int nsel = ts.target + 1;  // min(32, n)
             const int slot = ts.cnt_before + rank;
             if (slot < nsel) {
-              sm.win_e[row][slot] = ea;
+              sm.win_u[row][slot] = ua;
               sm.win_j[row][slot] = ja;
             }
           }
@@ -774,16 +777,16 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   // ---- E: outputs ---------------------------------------------------------------------------------
   for (int row = w; row < ROWS; row += NW) {
     const RowInfo ri = row_info(p, b, hkv, rb, row);
-    const unsigned bmx = __shfl(bitsmax, row);
+    const float mr = __shfl(m, row), ksr = __shfl(kscale, row);
     if (ri.ok) {
       const int nsel = min(32, ri.nvis);
       int rank = 0, jl = -1;
       if (lane < nsel) {
-        const float el = sm.win_e[row][lane];
+        const float ul = sm.win_u[row][lane];
         jl = sm.win_j[row][lane];
-        const unsigned Dl = bmx - __float_as_uint(el);
+        const unsigned Dl = dkey(ul, mr, ksr);
         for (int q = 0; q < nsel; ++q) {
-          const unsigned Dq = bmx - __float_as_uint(sm.win_e[row][q]);
+          const unsigned Dq = dkey(sm.win_u[row][q], mr, ksr);
           const int jq = sm.win_j[row][q];
           rank += (Dq < Dl) || (Dq == Dl && jq < jl);
         }
@@ -815,8 +818,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 
   // strict zeros: only rows whose smallest e' can be at or below Z' 2^-150 need a counting pass
   {
-    const unsigned emin_bits = bitsmin;
-    int need = (me.ok && __uint_as_float(emin_bits) <= thrz) ? 1 : 0;
+    int need = (me.ok && mn <= thr_u) ? 1 : 0;
     if (tid == 0) sm.flag = 0;
     __syncthreads();
     if (need) atomicOr(&sm.flag, 1);
@@ -830,7 +832,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = j0 + 4 * gq + i;
-          cnt += (j < nv && sc[t][i] <= thrz) ? 1 : 0;
+          cnt += (j < nv && sc[t][i] <= thr_u) ? 1 : 0;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -851,7 +853,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     const float pmul = invZ * kPScale;
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
-      const float pm = opaque(pmul);  // recomputed per half, not hoisted as one f16 pair per tile
+      const float pm = opaque(pmul), offq = opaque(off);  // recomputed per half, not hoisted per tile
       const int rq = opaque(r), gq = opaque(g);  // likewise the per-key V offsets
       f32x4 oacc[4];
 #pragma unroll
@@ -862,7 +864,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         if (j0 < kmax) {
         f16x4 pa;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pa[i] = (_Float16)(sc[t][i] * pm);
+        for (int i = 0; i < 4; ++i) pa[i] = (_Float16)(__builtin_amdgcn_exp2f(fmaxf(sc[t][i] + offq, -256.f)) * pm);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int c = half * 64 + db * 16 + rq;
@@ -1006,7 +1008,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         ref_tile(j0 + 16 * h2, u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pm = sc[t + h2][i] * invZ;
+          const float pm = __builtin_amdgcn_exp2f(fmaxf(sc[t + h2][i] + off, -256.f)) * invZ;
           pv[h2][i] = pm;
           tv += fabsf(pm - __builtin_amdgcn_exp2f(u[i] - mref) * invZr);
         }

@@ -1,0 +1,115 @@
+"""GPU parity of the quantized modes: MXFP8 row statistics (tiny workload) and attention over the
+packed 4-bit KV cache with the float32 recent window (decode-shaped GQA workload)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvprof_oracle as O
+from quantized_kv_amd import binding as B
+from quantized_kv_amd import inputs
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _np(d):
+    return {k: v.detach().cpu().numpy() for k, v in d.items() if isinstance(v, torch.Tensor)}
+
+
+def test_mxfp8_tiny(kvprof_lib):
+    Q, K, _ = inputs.tiny_inputs(1)
+    signs = inputs.hadamard_signs(4)
+    sg = torch.from_numpy(signs).to(DEV)
+    qd, kd = Q.to(DEV), K.to(DEV)
+    qc, qs = B.kvprof_pack_mxfp8(qd.reshape(-1, 128), sg)
+    kc, ks = B.kvprof_pack_mxfp8(kd.reshape(-1, 128), sg)
+    rb = [0, inputs.TINY_EARLY, inputs.TINY_N]
+    want = ("support", "top_mass", "top32", "strict_zero", "region_mass", "tv_qk", "argmax", "argmax_ref",
+            "p_zero_frac", "tv_p", "p_rowsum")
+    g = _np(B.run(qd, kd, want=want, mode=B.MODE_MXFP8, q_codes=qc, q_scales=qs, k_codes=kc, k_scales=ks,
+                  region_bounds=rb))
+    torch.cuda.synchronize()
+    for var in range(3):
+        sl = slice(var * 128, (var + 1) * 128)
+        ref = O.mx_row_stats(inputs.bf16_values(Q[var, 0]), inputs.bf16_values(K[var, 0]), signs,
+                             scale=128 ** -0.5, region_bounds=rb)
+        gv = {k: v[sl] for k, v in g.items()}
+        P.check_rows(gv, ref)
+        P.check_close("tv_qk", gv["tv_qk"], ref["tv_qk"], atol=P.MASS_ATOL)
+        P.check_close("tv_p", gv["tv_p"], ref["tv_p"], atol=P.MASS_ATOL)
+        P.check_close("p_rowsum", gv["p_rowsum"], ref["p_rowsum"], atol=P.MASS_ATOL)
+        # zero fraction: exact count except keys whose fp32 probability sits within the tie margin of
+        # the E4M3 underflow boundary (or in a block whose shared exponent is itself at a boundary)
+        for r in range(128):
+            p32 = ref["p"][r].astype(np.float32).astype(np.float64)
+            lo = hi = 0
+            for b0 in range(0, 128, 32):
+                blk = p32[b0:b0 + 32]
+                amax = blk.max()
+                e = O.e8m0_exponent(float(amax))
+                edge = any(abs(amax - 448 * 2.0 ** ee) <= 1e-5 * amax for ee in (e - 1, e))
+                x = blk * 2.0 ** -e
+                zero = (blk > 0) & (x <= 2.0 ** -10)
+                near = np.abs(x - 2.0 ** -10) <= 1e-5 * 2.0 ** -10
+                if edge:
+                    hi += int(np.sum(blk > 0))
+                else:
+                    lo += int(np.sum(zero & ~near))
+                    hi += int(np.sum(zero | near))
+            cnt = int(round(gv["p_zero_frac"][r] * 128))
+            assert lo <= cnt <= hi, (var, r, cnt, lo, hi)
+        for name, sc in (("argmax", ref["scores"]), ("argmax_ref", ref["ref_scores"])):
+            for r in range(128):
+                srt = np.sort(sc[r])[::-1]
+                if abs(srt[0] - srt[1]) < P.tie_margin(srt[0], srt[1]):
+                    continue
+                assert gv[name][r] == ref[name][r], (var, name, r)
+
+
+@pytest.mark.parametrize("R", [0, 16, 64])
+def test_attend_int4_decode(kvprof_lib, R):
+    Q, K, V = inputs.decode_inputs(5)
+    L, Mq = inputs.DECODE_L, inputs.DECODE_MQ
+    packed = B.kvprof_pack_int4kv(K.to(DEV), V.to(DEV), R)
+    rb = [0, L - R, L] if R > 0 else None
+    kw = dict(causal=True, q_pos0=L - Mq, region_bounds=rb)
+    want = ("top32", "o") + (("region_mass",) if R else ())
+    gq = _np(B.run(Q[None].to(DEV), None, want=want, attend=True, mode=B.MODE_INT4KV, kv_packed=packed,
+                   r_window=R, n_k=L, n_heads_kv=2, **kw))
+    gr = _np(B.run(Q[None].to(DEV), K[None].to(DEV), V[None].to(DEV), want=want, attend=True, **kw))
+    torch.cuda.synchronize()
+    qv = inputs.bf16_values(Q)
+    # the oracle unpacks the blobs it packs itself (the codec parity test pins them to the device's)
+    blobs = [O.pack_int4kv(inputs.bf16_values(K[h]), inputs.bf16_values(V[h]), R) for h in range(2)]
+    assert all(np.array_equal(bl, dev) for bl, dev in zip(blobs, packed.cpu().numpy()))
+    khat, vhat = zip(*[O.unpack_int4kv(bl) for bl in blobs])
+    kref, vref = inputs.bf16_values(K), inputs.bf16_values(V)
+    rows = np.r_[0:8, 120:128, 248:256]
+    for h in (0, 7, 8, 15):
+        sl = slice(h * Mq, (h + 1) * Mq)
+        refq = O.row_stats(qv[h], khat[h // 8], scale=128 ** -0.5, causal=True, q_pos0=L - Mq,
+                           region_bounds=rb, v=vhat[h // 8])
+        refr = O.row_stats(qv[h], kref[h // 8], scale=128 ** -0.5, causal=True, q_pos0=L - Mq,
+                           region_bounds=rb, v=vref[h // 8])
+        for which, g, ref in (("int4", gq, refq), ("bf16", gr, refr)):
+            print(f"decode R={R} head {h} {which}", flush=True)
+            gh = {k: v[sl][rows] for k, v in g.items()}
+            rh = {k: (v[rows] if getattr(v, "ndim", 0) >= 1 and len(v) == Mq else v) for k, v in ref.items()}
+            P.check_top32(gh["top32"], rh["scores"], rh["n_visible"])
+            P.check_o(gh["o"], rh["o"])
+            if R:
+                P.check_close("recent mass", gh["region_mass"][:, 1], rh["region_mass"][:, 1], atol=P.MASS_ATOL)
+    # comparison kernel: relative L2 and recall@32 of the GPU outputs
+    rel, rec, sums = B.kvprof_compare(torch.from_numpy(gq["o"]).to(DEV), torch.from_numpy(gr["o"]).to(DEV),
+                                      torch.from_numpy(gq["top32"]).to(DEV), torch.from_numpy(gr["top32"]).to(DEV))
+    torch.cuda.synchronize()
+    rel, rec, sums = rel.cpu().numpy(), rec.cpu().numpy(), sums.cpu().numpy()
+    ref_rel = np.linalg.norm(gq["o"].astype(np.float64) - gr["o"], axis=1) / np.linalg.norm(gr["o"].astype(np.float64), axis=1)
+    assert np.allclose(rel, ref_rel, rtol=1e-5)
+    ref_rec = np.array([O.recall32(a, b) for a, b in zip(gq["top32"], gr["top32"])])
+    assert np.array_equal(rec, ref_rec.astype(np.float32))
+    tensor_rel = np.sqrt(sums[0] / sums[1])
+    assert tensor_rel == pytest.approx(O.rel_l2(gq["o"].astype(np.float64), gr["o"].astype(np.float64)), rel=1e-6)
+    if R == 0:
+        assert 0.02 < tensor_rel < 0.3  # 4-bit K/V: error of the order of ten percent

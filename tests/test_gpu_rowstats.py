@@ -1,0 +1,163 @@
+"""GPU parity of kvprof_row_stats / kvprof_attend (bf16 mode) against the oracle, through the C ABI.
+
+Sizes span several 16-key tiles and several 16-row workgroups with ragged tails; the video-workload
+cases run at full size (6,240 keys) and compare a sample of rows the oracle can compute one by one."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvprof_oracle as O
+from quantized_kv_amd import binding as B
+from quantized_kv_amd import inputs
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+ALL = ("support", "top_mass", "top32", "strict_zero", "row_max", "row_lse")
+
+
+def _np(d):
+    return {k: v.detach().cpu().numpy() for k, v in d.items() if isinstance(v, torch.Tensor)}
+
+
+def _head(g, b, h, Hq, Mq):
+    out = {}
+    for k, v in g.items():
+        if k in ("heatmap", "heatmap_mean", "hist"):
+            continue
+        out[k] = v.reshape((-1, Hq, Mq) + v.shape[1:])[b, h]
+    return out
+
+
+def _compare_all(g, Q, K, V, *, scale, Hkv, heads=None, rows=None, **kw):
+    Bn, Hq, Mq, _ = Q.shape
+    grp = Hq // Hkv
+    qv, kv = inputs.bf16_values(Q), inputs.bf16_values(K)
+    vv = inputs.bf16_values(V) if V is not None else None
+    for b in range(Bn):
+        for h in (range(Hq) if heads is None else heads):
+            qq = qv[b, h] if rows is None else qv[b, h][rows]
+            ref = O.row_stats(qq, kv[b, h // grp], scale=scale, v=None if vv is None else vv[b, h // grp], **kw)
+            gh = _head(g, b, h, Hq, Mq)
+            if rows is not None:
+                gh = {k: v[rows] for k, v in gh.items()}
+            P.check_rows(gh, ref)
+
+
+def test_tiny_variants_all_stats_and_o(kvprof_lib):
+    Q, K, V = inputs.tiny_inputs(1)
+    rb = [0, inputs.TINY_EARLY, inputs.TINY_N]
+    g = B.run(Q.to(DEV), K.to(DEV), V.to(DEV), want=ALL + ("region_mass", "o"), region_bounds=rb)
+    torch.cuda.synchronize()
+    _compare_all(_np(g), Q, K, V, scale=128 ** -0.5, Hkv=1, region_bounds=rb)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_gqa_bias_frames_heatmap_hist(kvprof_lib, causal):
+    rng = np.random.default_rng(11)
+    Bn, Hq, Hkv, Mq, Sk = 2, 4, 2, 37, 1000
+    Q, K, V = inputs.generic_inputs(21, (Bn, Hq, Mq, 128), (Bn, Hkv, Sk, 128), q_scale=1.5)
+    bias = rng.standard_normal(Sk).astype(np.float32)
+    rb = [0, 250, 600, 1000]
+    groups = (np.arange(Mq) % 5).astype(np.int32)
+    kw = dict(scale=0.09, key_bias=torch.from_numpy(bias).to(DEV), causal=causal, q_pos0=Sk - Mq,
+              region_bounds=rb, frame_len=100, n_frames=10, row_group=torch.from_numpy(groups).to(DEV),
+              n_groups=5)
+    g = B.run(Q.to(DEV), K.to(DEV), V.to(DEV), want=ALL + ("region_mass", "frame_mass", "o"), heatmap=True,
+              hist=True, attend=True, **kw)
+    torch.cuda.synchronize()
+    gn = _np(g)
+    _compare_all(gn, Q, K, V, scale=0.09, Hkv=Hkv, key_bias=bias, causal=causal, q_pos0=Sk - Mq,
+                 region_bounds=rb, frame_len=100, n_frames=10)
+    # heatmap from the GPU's own frame masses vs the oracle's definition
+    fm = gn["frame_mass"].reshape(Bn, Hq, Mq, 10)
+    for b in range(Bn):
+        for h in range(Hq):
+            P.check_close("heatmap", gn["heatmap"][b, h], O.heatmap(fm[b, h], groups, 5), atol=1e-6)
+        P.check_close("heatmap_mean", gn["heatmap_mean"][b], gn["heatmap"][b].mean(axis=0), atol=1e-6)
+    # histograms: counts per record sum to its rows; bins equal the oracle's binning of the GPU values
+    hs = gn["hist"]
+    sup = gn["support"].reshape(Bn, -1)
+    reg = gn["region_mass"].reshape(Bn, -1, 3)
+    for b in range(Bn):
+        assert hs[b].sum(axis=1).tolist() == [Hq * Mq] * 4
+        assert np.array_equal(hs[b, 0], O.histogram100(sup[b].astype(np.float64)))
+        for q in range(3):
+            assert np.array_equal(hs[b, 1 + q], O.histogram100(reg[b, :, q].astype(np.float64)))
+
+
+def test_special_rows(kvprof_lib):
+    """Uniform rows (Q = 0), one-hot rows (strict zeros), duplicated keys (ties to low indices)."""
+    Sk = 300
+    rng = np.random.default_rng(5)
+    q = np.zeros((1, 1, 48, 128), np.float32)
+    q[0, 0, 16:] = rng.standard_normal((32, 128)) * 3
+    k = rng.standard_normal((1, 1, Sk, 128)).astype(np.float32)
+    k[0, 0, 100:140] = k[0, 0, 7]  # duplicates of key 7
+    q[0, 0, 16:32] = k[0, 0, 7] * 4  # rows that prefer key 7 and its copies
+    Q, K = inputs.to_bf16(q), inputs.to_bf16(k)
+    bias = np.zeros(Sk, np.float32)
+    bias[299] = 200.0  # one-hot rows for the zero-query rows ... and near-one-hot elsewhere
+    for b_ in (None, bias):
+        kw = {} if b_ is None else dict(key_bias=torch.from_numpy(b_).to(DEV))
+        g = _np(B.run(Q.to(DEV), K.to(DEV), want=ALL, scale=0.1, **kw))
+        torch.cuda.synchronize()
+        ref = O.row_stats(inputs.bf16_values(Q)[0, 0], inputs.bf16_values(K)[0, 0], scale=0.1, key_bias=b_)
+        P.check_rows(g, ref)
+        if b_ is None:
+            assert np.allclose(g["support"][:16], 1.0, atol=1e-5)
+            assert np.allclose(g["top_mass"][:16], [0.01, 0.05, 0.10], atol=1e-6)
+            assert (g["top32"][:16] == np.arange(32)).all()
+        else:
+            assert (g["strict_zero"][:16] == Sk - 1).all()
+
+
+def test_deterministic(kvprof_lib):
+    Q, K, V = inputs.generic_inputs(3, (1, 2, 40, 128), (1, 2, 700, 128))
+    a = _np(B.run(Q.to(DEV), K.to(DEV), V.to(DEV), want=ALL + ("o",), attend=True))
+    b = _np(B.run(Q.to(DEV), K.to(DEV), V.to(DEV), want=ALL + ("o",), attend=True))
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+VIDEO_KW = dict(region_bounds=inputs.VIDEO_REGION_BOUNDS, frame_len=inputs.LF_TOKENS,
+                n_frames=inputs.N_KEY_FRAMES)
+
+
+def test_video_sampled_record(kvprof_lib):
+    """Sampled-query record 0 at full size (32 heads x 96 queries x 6,240 keys); oracle on 3 heads."""
+    rec = inputs.video_record(0, with_v=False, sampled=True)
+    bias = inputs.video_key_bias()
+    groups = inputs.video_sample_groups()
+    g = B.run(rec.q[None].to(DEV), rec.k[None].to(DEV), want=ALL + ("region_mass", "frame_mass"),
+              scale=128 ** -0.5, key_bias=torch.from_numpy(bias).to(DEV),
+              row_group=torch.from_numpy(groups).to(DEV), n_groups=6, heatmap=True, hist=True, **VIDEO_KW)
+    torch.cuda.synchronize()
+    gn = _np(g)
+    _compare_all(gn, rec.q[None], rec.k[None], None, scale=128 ** -0.5, Hkv=32, heads=[0, 13, 31],
+                 key_bias=bias, **VIDEO_KW)
+    hm = gn["heatmap"][0]
+    assert hm.shape == (32, 6, 16)
+    assert np.allclose(hm.sum(axis=2), 1.0, atol=2e-3)
+    assert gn["hist"][0].sum(axis=1).tolist() == [3072] * 4
+
+
+def test_video_full_rows_sample(kvprof_lib):
+    """Full-row record 0 (2,340 queries x 6,240 keys) on 2 heads; oracle on a row sample; the sampled
+    workload's rows equal the full workload's rows at the grid positions (row independence)."""
+    rec = inputs.video_record(0, heads=2, with_v=False)
+    bias = inputs.video_key_bias()
+    g = _np(B.run(rec.q[None].to(DEV), rec.k[None].to(DEV), want=ALL + ("region_mass", "frame_mass"),
+                  scale=128 ** -0.5, key_bias=torch.from_numpy(bias).to(DEV), **VIDEO_KW))
+    torch.cuda.synchronize()
+    rows = np.r_[0:20, 1000:1010, 2320:2340]
+    _compare_all(g, rec.q[None], rec.k[None], None, scale=128 ** -0.5, Hkv=2, rows=rows, key_bias=bias,
+                 **VIDEO_KW)
+    srec = inputs.video_record(0, heads=2, with_v=False, sampled=True)
+    gs = _np(B.run(srec.q[None].to(DEV), srec.k[None].to(DEV), want=ALL + ("region_mass", "frame_mass"),
+                   scale=128 ** -0.5, key_bias=torch.from_numpy(bias).to(DEV), **VIDEO_KW))
+    torch.cuda.synchronize()
+    sel = inputs.video_sample_rows()
+    for k in gs:
+        full = g[k].reshape((2, 2340) + g[k].shape[1:])[:, sel].reshape(gs[k].shape)
+        assert np.array_equal(full, gs[k]), k
