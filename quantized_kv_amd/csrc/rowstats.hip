@@ -37,6 +37,7 @@ constexpr int NT = 4;    // selected ranks per row
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kPScale = 32768.f;  // P is fed to the f16 MFMA as p * 2^15
+constexpr int kRing = 3;  // K tiles in flight per wave (bf16 path): LDS ring filled by direct loads
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -61,7 +62,10 @@ struct Sel {
   unsigned hmass[ROWS][HB];
   float ce[ROWS][CAP];  // candidate scores u
   int cj[ROWS][CAP];
-  float sorted_e[ROWS][CAP];
+  union {
+    float sorted_e[ROWS][CAP];  // slow path: candidate e' by rank
+    int crank[ROWS][CAP];       // fast path: rank of a candidate inside its level-1 bin
+  };
 };
 
 struct Smem {
@@ -72,7 +76,7 @@ struct Smem {
   float segpart[NW][ROWS][kSegPerWave];
   float segmass[ROWS][kMaxSeg];
   int cs0[NW];
-  float r_z[ROWS], r_e[ROWS];
+  float r_z[ROWS], r_e[ROWS], r_m[ROWS], r_mn[ROWS];
   int flag;
   TState ts[ROWS][NT];
   float tmass[ROWS][3];
@@ -81,9 +85,11 @@ struct Smem {
   int win_j[ROWS][32];
   int top0[ROWS];
   u32x4 qs[ROWS][16];  // Q rows as 16-byte chunks (B operand of S^T = K Q^T)
+  float bias2[KVPROF_MAX_KEYS];  // key bias * log2(e)
   union {
     Sel sel;
     float ored[NW / 2][ROWS][64];
+    u32x4 ring[NW][kRing][4][64];  // per wave: kRing K tiles x 4 k-steps x 64 lanes (A fragments)
   } u;
 };
 
@@ -316,8 +322,8 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   const int hkv = (bid / nrb) % p.n_heads_kv;
   const int b = bid / (nrb * p.n_heads_kv);
 
-  const RowInfo me = row_info(p, b, hkv, rb, r);
-  const int nvis = me.nvis;
+  const RowInfo me0 = row_info(p, b, hkv, rb, r);
+  const int nvis = me0.nvis;
   // workgroup-uniform extent of visible keys
   int kmax = nvis;
   for (int o = 1; o < 16; o <<= 1) kmax = max(kmax, __shfl_xor(kmax, o));
@@ -333,27 +339,25 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     rk = make_rsrc(p.kv_packed + kvh * p.blob_bytes, p.blob_bytes);
     rv = rk;
   }
-  const rsrc_t rbias = make_rsrc(p.key_bias ? (const void*)p.key_bias : (const void*)p.q,
-                                 p.key_bias ? (size_t)p.n_k * 4 : 0);
   Int4Layout L{};
   if (KSRC == KSRC_INT4) L = int4_layout(p.n_k, KVPROF_HEAD_DIM, p.r_window);
 
   // clear the shared accumulators
   for (int i = tid; i < NW * ROWS * kSegPerWave; i += WGT) (&sm.segpart[0][0][0])[i] = 0.f;
-  for (int i = tid; i < ROWS * HB * 2; i += WGT) (&sm.u.sel.hcnt[0][0])[i] = 0u;
 
   // Q rows of the workgroup into LDS (wave 0): chunk c of row r holds dims 8c .. 8c+7
   if (w == 0) {
 #pragma unroll
     for (int c = g; c < 16; c += 4) {
       u32x4 v = zero4();
-      if (me.ok) {
-        v = *reinterpret_cast<const u32x4*>(p.q + (size_t)me.grow * KVPROF_HEAD_DIM + 8 * c);
+      if (me0.ok) {
+        v = *reinterpret_cast<const u32x4*>(p.q + (size_t)me0.grow * KVPROF_HEAD_DIM + 8 * c);
         if (KSRC == KSRC_INT4) v = bf16x8_to_f16x8_bits(v);
       }
       sm.qs[r][c] = v;
     }
   }
+  for (int j = tid; j < p.n_k; j += WGT) sm.bias2[j] = p.key_bias ? p.key_bias[j] * kLog2e : 0.f;
   __syncthreads();
 
   // ---- A: scores ---------------------------------------------------------------------------------
@@ -362,32 +366,58 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   float umax = -INFINITY, umin = INFINITY;
   // The scheduling barrier at the end of each tile keeps the compiler from hoisting every tile's
   // loads, which would push the score registers out to scratch.
+  if (KSRC == KSRC_BF16) {
+    // Direct global->LDS loads (no VGPRs): tile t of this wave goes to ring slot t % kRing, each lane's
+    // 16 bytes landing at lane * 16, which is exactly its A-fragment. The compiler does not track
+    // these writes, so the wait before reading a slot is explicit: loads retire in issue order, and at
+    // most 4 * (kRing - 1) loads (the later tiles) may still be outstanding.
+#pragma unroll
+    for (int t = 0; t < kRing - 1 && t < TPW; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)&sm.u.ring[w][t % kRing][ks][0],
+                                                 16, (unsigned)((kbase + t * 16 + r) * KVPROF_HEAD_DIM + ks * 32 + 8 * g) * 2u, 0, 0, 0);
+  }
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int j0 = kbase + t * 16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (j0 < kmax) {
+    if (KSRC == KSRC_BF16) {
+      if (t + kRing - 1 < TPW) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rk, (__attribute__((address_space(3))) void*)&sm.u.ring[w][(t + kRing - 1) % kRing][ks][0], 16,
+              (unsigned)((j0 + (kRing - 1) * 16 + r) * KVPROF_HEAD_DIM + ks * 32 + 8 * g) * 2u, 0, 0, 0);
+      }
+      constexpr int later = 4 * (kRing - 1);
+      const int pend = (TPW - 1 - t) < (kRing - 1) ? 4 * (TPW - 1 - t) : later;
+      // s_waitcnt vmcnt(pend), expcnt / lgkmcnt left alone (gfx9 encoding)
+      switch (pend) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+      }
+      if (j0 < kmax) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          acc = mfma_step<KSRC>(sm.u.ring[w][t % kRing][ks][lane], sm.qs[r][ks * 4 + g], acc);
+      }
+    } else if (j0 < kmax) {
       u32x4 kf[4], kl[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[ks] = load_k<KSRC>(p, rk, L, j0 + r, ks * 32 + 8 * g, KSRC == KSRC_INT4 ? &kl[ks] : nullptr);
+      for (int ks = 0; ks < 4; ++ks) kf[ks] = load_k<KSRC>(p, rk, L, j0 + r, ks * 32 + 8 * g, &kl[ks]);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         acc = mfma_step<KSRC>(kf[ks], sm.qs[r][ks * 4 + g], acc);
-        if (KSRC == KSRC_INT4) acc = mfma_step<KSRC>(kl[ks], sm.qs[r][ks * 4 + g], acc);
+        acc = mfma_step<KSRC>(kl[ks], sm.qs[r][ks * 4 + g], acc);
       }
     }
     float bias[4] = {0.f, 0.f, 0.f, 0.f};
     if (p.key_bias && j0 < kmax) {
-      const int jb = j0 + 4 * g;
-      if (jb + 3 < p.n_k) {
-        f32x4 bv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rbias, (unsigned)jb * 4u, 0, 0));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bias[i] = bv[i] * kLog2e;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          bias[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbias, (unsigned)(jb + i) * 4u, 0, 0)) * kLog2e;
-      }
+      for (int i = 0; i < 4; ++i) bias[i] = (j0 + 4 * g + i < p.n_k) ? sm.bias2[j0 + 4 * g + i] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -423,9 +453,13 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     m = fmaxf(m, sm.red_a[ww][r]);
     mn = fminf(mn, sm.red_b[ww][r]);
   }
-  if (!me.ok) {
+  if (!me0.ok) {
     m = 0.f;
     mn = 0.f;
+  }
+  if (w == 0 && g == 0) {
+    sm.r_m[r] = m;
+    sm.r_mn[r] = mn;
   }
 
   // ---- B: exponentials, entropy sum, segment masses -----------------------------------------------
@@ -477,6 +511,9 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   if (kbase < kmax && cs < p.n_seg) flush(acc_seg, cs);
   esum = row_sum4(esum);
   if (g == 0) sm.red_e[w][r] = esum;
+  // the histogram shares LDS with the phase-A load ring: clear it only now (every ring load has
+  // completed: the last tile waited for vmcnt(0))
+  for (int i = tid; i < ROWS * HB * 2; i += WGT) (&sm.u.sel.hcnt[0][0])[i] = 0u;
   __syncthreads();
 
   // ---- per-row finalisation of B (wave w handles rows w and w + 8) --------------------------------------------
@@ -507,14 +544,21 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     }
   }
   __syncthreads();
-  const float Zp = sm.r_z[r];
-  const float invZ = 1.f / Zp;
-  // row constants for the selection (every lane of the row computes the same values)
-  const float kscale = (m - mn > 0.f) ? 4294967040.f / (m - mn) : 0.f;
-  const float inv_fx = 2147483648.f / Zp;
-
+  // Row constants are read back from LDS where they are used (they would otherwise stay live in
+  // registers next to the scores for the rest of the kernel).
+  auto rc_m = [&]() { return sm.r_m[r]; };
+  auto rc_z = [&]() { return sm.r_z[r]; };
+  auto rc_ks = [&]() {
+    const float d = sm.r_m[r] - sm.r_mn[r];
+    return d > 0.f ? 4294967040.f / d : 0.f;
+  };
+  auto rc_fx = [&]() { return 2147483648.f / sm.r_z[r]; };
   // p <= 2^-150 (an fp32 zero) <=> u - max + 64 - log2 Z' <= -150
-  const float thr_u = m + log2f(Zp) - 214.f;
+  auto rc_thr = [&]() { return sm.r_m[r] + log2f(sm.r_z[r]) - 214.f; };
+  auto row_ks = [&](int row) {
+    const float d = sm.r_m[row] - sm.r_mn[row];
+    return d > 0.f ? 4294967040.f / d : 0.f;
+  };
 
   // region / frame / scalar outputs and target setup (wave w handles rows w and w + 8)
   for (int row = w; row < ROWS; row += NW) {
@@ -565,6 +609,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   // ---- C: level-1 histogram -------------------------------------------------------------------------
   {
   const int gq = opaque(g), nv = opaque(nvis);
+  const float mq = rc_m(), ksq = rc_ks(), offq = 64.f - mq, ifx = rc_fx();
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int j0 = kbase + t * 16;
@@ -573,10 +618,10 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       const int j = j0 + 4 * gq + i;
       if (j < nv) {
         const float u = sc[t][i];
-        const float e = __builtin_amdgcn_exp2f(fmaxf(u + off, -256.f));
-        const int dig = (int)(dkey(u, m, kscale) >> kSh);
+        const float e = __builtin_amdgcn_exp2f(fmaxf(u + offq, -256.f));
+        const int dig = (int)(dkey(u, mq, ksq) >> kSh);
         atomicAdd(&sm.u.sel.hcnt[r][dig], 1u);
-        atomicAdd(&sm.u.sel.hmass[r][dig], (unsigned)__builtin_rintf(e * inv_fx));
+        atomicAdd(&sm.u.sel.hmass[r][dig], (unsigned)__builtin_rintf(e * ifx));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -586,6 +631,129 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   for (int row = w; row < ROWS; row += NW) scan_row(sm, row, lane, 0);
   __syncthreads();
 
+  // ---- D: exact ranks ------------------------------------------------------------------------------
+  // Fast path (the common case): every target's boundary bin holds at most CAP keys and the distinct
+  // boundary bins of a row hold at most CAP keys together. One pass then gathers, for every row, the
+  // keys of its boundary bins (candidates) and the keys ranked above the top-32 boundary (winners);
+  // candidates are ranked inside their bin by (key, index). Masses are summed as fixed-point integers,
+  // whose sum does not depend on the order. Otherwise the slow path narrows each target with further
+  // radix levels.
+  if (tid == 0) sm.flag = 0;
+  __syncthreads();
+  for (int row = w; row < ROWS; row += NW) {
+    if (lane == 0) {
+      int tot = 0, bad = 0;
+      for (int t = 0; t < NT; ++t) {
+        const TState& ts = sm.ts[row][t];
+        if (ts.width == 0) continue;  // invalid row
+        if (!ts.resolved) bad = 1;
+        bool seen = false;
+        for (int q = 0; q < t; ++q) seen |= sm.ts[row][q].width > 0 && sm.ts[row][q].prefix == ts.prefix;
+        if (!seen) tot += ts.cnt_in;
+      }
+      if (bad || tot > CAP) atomicOr(&sm.flag, 1);
+    }
+  }
+  if (tid < ROWS) {
+    sm.ncand[tid] = 0;
+    sm.nwin[tid] = 0;
+  }
+  __syncthreads();
+  const bool slow_path = sm.flag != 0;
+  if (!slow_path) {
+    {
+      // boundary bins of this lane's row (level-1 digits)
+      int bq[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) bq[t] = sm.ts[r][t].width > 0 ? (int)sm.ts[r][t].prefix : -1;
+      const int bmax = max(max(bq[0], bq[1]), max(bq[2], bq[3]));
+      const int gq = opaque(g), nv = opaque(nvis);
+      const float mq = rc_m(), ksq = rc_ks();
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) {
+        const int j0 = kbase + tt * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + 4 * gq + i;
+          const float u = sc[tt][i];
+          const unsigned D = dkey(u, mq, ksq);
+          const int dig = (int)(D >> kSh);
+          if (j < nv && dig <= bmax) {
+            // a key can be both: ranked above the top-32 boundary and inside the boundary bin of a
+            // 1/5/10 % rank (at small n those ranks lie above rank 31)
+            if (dig < bq[0]) {
+              const int slot = atomicAdd(&sm.nwin[r], 1);
+              if (slot < 32) {
+                sm.win_u[r][slot] = u;
+                sm.win_j[r][slot] = j;
+              }
+            }
+            if (dig == bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3]) {
+              const int slot = atomicAdd(&sm.ncand[r], 1);
+              if (slot < CAP) {
+                sm.u.sel.ce[r][slot] = u;
+                sm.u.sel.cj[r][slot] = j;
+              }
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+    // rank every candidate inside its bin
+    for (int row = w; row < ROWS; row += NW) {
+      const float mr = sm.r_m[row], ksr = row_ks(row);
+      const int c = min(sm.ncand[row], CAP);
+      for (int a = lane; a < c; a += 64) {
+        const unsigned Da = dkey(sm.u.sel.ce[row][a], mr, ksr);
+        const int ja = sm.u.sel.cj[row][a];
+        const unsigned dga = Da >> kSh;
+        int rank = 0;
+        for (int q = 0; q < c; ++q) {
+          const unsigned Dq = dkey(sm.u.sel.ce[row][q], mr, ksr);
+          const int jq = sm.u.sel.cj[row][q];
+          rank += ((Dq >> kSh) == dga) && ((Dq < Da) || (Dq == Da && jq < ja));
+        }
+        sm.u.sel.crank[row][a] = rank;
+      }
+    }
+    __syncthreads();
+    for (int row = w; row < ROWS; row += NW) {
+      const float mr = sm.r_m[row], ksr = row_ks(row), ifx = 2147483648.f / sm.r_z[row];
+      const RowInfo ri = row_info(p, b, hkv, rb, row);
+      const int c = min(sm.ncand[row], CAP);
+      unsigned acc[NT] = {0u, 0u, 0u, 0u};
+      for (int a = lane; a < c; a += 64) {
+        const float ua = sm.u.sel.ce[row][a];
+        const unsigned dga = dkey(ua, mr, ksr) >> kSh;
+        const int rk = sm.u.sel.crank[row][a];
+        const float ea = __builtin_amdgcn_exp2f(fmaxf(ua + (64.f - mr), -256.f));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const TState& ts = sm.ts[row][t];
+          if (ts.width == 0 || (unsigned)ts.prefix != dga) continue;
+          const int rr = ts.target - ts.cnt_before;
+          if (t == 0) {
+            if (rk <= rr) {  // ranks 0..target of the top-32 list
+              sm.win_u[row][ts.cnt_before + rk] = ua;
+              sm.win_j[row][ts.cnt_before + rk] = sm.u.sel.cj[row][a];
+            }
+          } else {
+            if (rk < rr) acc[t] += (unsigned)__builtin_rintf(ea * ifx);
+            if (rk == rr) acc[t] += (unsigned)__builtin_rintf(ts.frac * ea * ifx);
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 1; t < NT; ++t) {
+        unsigned x = acc[t];
+        for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+        if (lane == 0 && ri.ok) sm.tmass[row][t - 1] = (float)(sm.ts[row][t].mass_before + x) * 0x1p-31f;
+      }
+    }
+    __syncthreads();
+  } else {
   // ---- D: refine and gather, one target at a time --------------------------------------------------
 #pragma unroll 1
   for (int t = 0; t < NT; ++t) {
@@ -609,8 +777,8 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       __syncthreads();
       if (active_row) {
         const int gq = opaque(g), nv = opaque(nvis);
-        const float mq = opaque(m), ksq = opaque(kscale), offq = opaque(off);
-        const float ifx = opaque(inv_fx);  // keeps the per-key masses from being hoisted out of the level loop
+        const float mq = rc_m(), ksq = rc_ks(), offq = 64.f - mq;
+        const float ifx = rc_fx();
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const int j0 = kbase + tt * 16;
@@ -689,10 +857,10 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     __syncthreads();
     {
       const TState tsr = sm.ts[r][t];
-      const bool rowok = me.ok && tsr.width > 0;
+      const bool rowok = nvis > 0 && tsr.width > 0;
       if (rowok) {
         const int gq = opaque(g), nv = opaque(nvis);
-        const float mq = opaque(m), ksq = opaque(kscale);
+        const float mq = rc_m(), ksq = rc_ks();
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const int j0 = kbase + tt * 16;
@@ -728,7 +896,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     for (int row = w; row < ROWS; row += NW) {
       const TState ts = sm.ts[row][t];
       const int c = min(sm.ncand[row], CAP);
-      const float mr = __shfl(m, row), ksr = __shfl(kscale, row);  // lane `row` holds that row
+      const float mr = sm.r_m[row], ksr = row_ks(row);
       if (ts.width > 0) {
         for (int a = lane; a < c; a += 64) {
           const float ua = sm.u.sel.ce[row][a];
@@ -774,10 +942,12 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     __syncthreads();
   }
 
+  }
+
   // ---- E: outputs ---------------------------------------------------------------------------------
   for (int row = w; row < ROWS; row += NW) {
     const RowInfo ri = row_info(p, b, hkv, rb, row);
-    const float mr = __shfl(m, row), ksr = __shfl(kscale, row);
+    const float mr = sm.r_m[row], ksr = row_ks(row);
     if (ri.ok) {
       const int nsel = min(32, ri.nvis);
       int rank = 0, jl = -1;
@@ -810,15 +980,17 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   }
   {
     // row max / lse: the lane of row r in wave 0 writes them
-    if (w == 0 && g == 0 && me.ok) {
-      if (p.row_max) p.row_max[me.grow] = m * kLn2;
-      if (p.row_lse) p.row_lse[me.grow] = (m + log2f(Zp) - 64.f) * kLn2;
+    const RowInfo me2 = row_info(p, b, hkv, rb, r);
+    if (w == 0 && g == 0 && me2.ok) {
+      if (p.row_max) p.row_max[me2.grow] = rc_m() * kLn2;
+      if (p.row_lse) p.row_lse[me2.grow] = (rc_m() + log2f(rc_z()) - 64.f) * kLn2;
     }
   }
 
   // strict zeros: only rows whose smallest e' can be at or below Z' 2^-150 need a counting pass
   {
-    int need = (me.ok && mn <= thr_u) ? 1 : 0;
+    const float thr_u = rc_thr();
+    int need = (nvis > 0 && sm.r_mn[r] <= thr_u) ? 1 : 0;
     if (tid == 0) sm.flag = 0;
     __syncthreads();
     if (need) atomicOr(&sm.flag, 1);
@@ -840,20 +1012,21 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     cnt = row_isum4(cnt);
     if (g == 0) sm.red_i[w][r] = cnt;
     __syncthreads();
-    if (w == 0 && g == 0 && me.ok) {
+    const RowInfo me3 = row_info(p, b, hkv, rb, r);
+    if (w == 0 && g == 0 && me3.ok) {
       int tot = 0;
       for (int ww = 0; ww < NW; ++ww) tot += sm.red_i[ww][r];
-      if (p.strict_zero) p.strict_zero[me.grow] = tot;
-      if (MX && p.argmax) p.argmax[me.grow] = sm.top0[r];
+      if (p.strict_zero) p.strict_zero[me3.grow] = tot;
+      if (MX && p.argmax) p.argmax[me3.grow] = sm.top0[r];
     }
   }
 
   // ---- O = P.V --------------------------------------------------------------------------------------
   if (p.o) {
-    const float pmul = invZ * kPScale;
+    const float pmul = kPScale / rc_z();
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
-      const float pm = opaque(pmul), offq = opaque(off);  // recomputed per half, not hoisted per tile
+      const float pm = opaque(pmul), offq = opaque(64.f - rc_m());  // recomputed per half, not hoisted per tile
       const int rq = opaque(r), gq = opaque(g);  // likewise the per-key V offsets
       f32x4 oacc[4];
 #pragma unroll
@@ -910,6 +1083,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   // ---- MXFP8 mode: bf16 reference row and the probability path ------------------------------------
   if (MX) {
     __syncthreads();
+    const RowInfo me = row_info(p, b, hkv, rb, r);
     const rsrc_t rkr = make_rsrc(p.k_ref + kvh * p.n_k * KVPROF_HEAD_DIM, head_bytes);
     u32x4 qr[4];
 #pragma unroll
@@ -927,7 +1101,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = j0 + 4 * g + i;
-        float bb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbias, (unsigned)j * 4u, 0, 0)) * kLog2e;
+        float bb = (j < p.n_k) ? sm.bias2[j] : 0.f;
         u[i] = j < nvis ? fmaf(acc[i], p.scale_log2, bb) : -INFINITY;
       }
     };
@@ -1008,7 +1182,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         ref_tile(j0 + 16 * h2, u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pm = __builtin_amdgcn_exp2f(fmaxf(sc[t + h2][i] + off, -256.f)) * invZ;
+          const float pm = __builtin_amdgcn_exp2f(fmaxf(sc[t + h2][i] + (64.f - rc_m()), -256.f)) / rc_z();
           pv[h2][i] = pm;
           tv += fabsf(pm - __builtin_amdgcn_exp2f(u[i] - mref) * invZr);
         }
@@ -1078,7 +1252,7 @@ hipError_t launch_t(const RowStatsParams& p, hipStream_t s) {
 
 int row_stats_tpw_for(int n_k, bool mx) {
   const int need = (n_k + NW * 16 - 1) / (NW * 16);
-  static const int kT[] = {1, 2, 4, 8, 16, 24, 32, 40, 50};
+  static const int kT[] = {1, 2, 4, 8, 16, 24, 32, 40, 49};
   static const int kTmx[] = {2, 4, 8, 16};
   if (mx) {
     for (int t : kTmx)
@@ -1110,7 +1284,7 @@ hipError_t launch_row_stats(const RowStatsParams& p, int tpw, int ksrc, bool mx,
       case 24: return launch_t<24, KSRC_INT4, false>(p, s);
       case 32: return launch_t<32, KSRC_INT4, false>(p, s);
       case 40: return launch_t<40, KSRC_INT4, false>(p, s);
-      case 50: return launch_t<50, KSRC_INT4, false>(p, s);
+      case 49: return launch_t<49, KSRC_INT4, false>(p, s);
       default: return hipErrorInvalidValue;
     }
   }
@@ -1123,7 +1297,7 @@ hipError_t launch_row_stats(const RowStatsParams& p, int tpw, int ksrc, bool mx,
     case 24: return launch_t<24, KSRC_BF16, false>(p, s);
     case 32: return launch_t<32, KSRC_BF16, false>(p, s);
     case 40: return launch_t<40, KSRC_BF16, false>(p, s);
-    case 50: return launch_t<50, KSRC_BF16, false>(p, s);
+    case 49: return launch_t<49, KSRC_BF16, false>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
