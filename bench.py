@@ -1,6 +1,7 @@
 """Benchmark of the KV-cache attention row profiler on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload sampled|full_rows|decode] [--no-cpu-baseline]
+    python bench.py --copy-calibration     # 1 GiB device copy, for scaling the HBM byte counters
 
 A step is one kvprof_row_stats call over the whole workload with every statistic the workload
 reports, inputs already resident in HBM:
@@ -39,6 +40,8 @@ def parse():
     ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode"])
     ap.add_argument("--records", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 1 GiB device copy instead (counter calibration)")
     return ap.parse_args()
 
 
@@ -53,6 +56,26 @@ def video_inputs(n_records: int, sampled: bool, dev):
         qs.append(rec.q.to(dev))
         ks.append(rec.k.to(dev))
     return torch.stack(qs), torch.stack(ks)
+
+
+KERNEL_SOURCES = ("quantized_kv_amd/csrc/rowstats.hip", "quantized_kv_amd/csrc/kvprof_device.h",
+                  "quantized_kv_amd/csrc/kvprof_internal.h")
+COUNTERS = os.path.join(ROOT, "profiles", "row_kernel_video_sampled_counters.json")
+
+
+def measured_traffic():
+    """HBM bytes per row-kernel launch from the committed FETCH_SIZE / WRITE_SIZE counter runs (scaled
+    by a plain copy's reading), or None when the kernel sources changed since they were taken."""
+    import hashlib
+
+    if not os.path.exists(COUNTERS):
+        return None
+    rec = json.load(open(COUNTERS))
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return rec["traffic_bytes_per_dispatch"] if rec.get("kernel_sources_sha256") == h.hexdigest() else None
 
 
 def time_it(fn, steps, warmup, stream):
@@ -71,27 +94,43 @@ def time_it(fn, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps  # ms per call
 
 
-def cpu_baseline_video(n_heads: int, sampled: bool):
-    """The oracle, as it stands, on record 0 restricted to n_heads heads (one BLAS thread)."""
+def cpu_baseline_video(n_records: int, sampled: bool):
+    """The oracle, as it stands, on the first n_records records (all heads), one BLAS thread."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import kvprof_oracle as O
     from quantized_kv_amd import inputs
 
-    rec = inputs.video_record(0, heads=n_heads, with_v=False, sampled=sampled)
-    q, k = inputs.bf16_values(rec.q), inputs.bf16_values(rec.k)
     bias = inputs.video_key_bias().astype(np.float64)
-    with threadpool_limits(1):
-        t = time.perf_counter()
-        rows = 0
-        for h in range(n_heads):
-            O.row_stats(q[h], k[h], scale=128 ** -0.5, key_bias=bias, region_bounds=inputs.VIDEO_REGION_BOUNDS,
-                        frame_len=inputs.LF_TOKENS, n_frames=inputs.N_KEY_FRAMES)
-            rows += q.shape[1]
-        dt = time.perf_counter() - t
-    return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"record 0, {n_heads} heads x {q.shape[1]} queries x 6240 keys ({rows} rows, {dt:.1f} s)"}
+    dt, rows = 0.0, 0
+    for r in range(n_records):
+        rec = inputs.video_record(r, with_v=False, sampled=sampled)
+        q, k = inputs.bf16_values(rec.q), inputs.bf16_values(rec.k)
+        with threadpool_limits(1):
+            t = time.perf_counter()
+            for h in range(q.shape[0]):
+                O.row_stats(q[h], k[h], scale=128 ** -0.5, key_bias=bias,
+                            region_bounds=inputs.VIDEO_REGION_BOUNDS, frame_len=inputs.LF_TOKENS,
+                            n_frames=inputs.N_KEY_FRAMES)
+                rows += q.shape[1]
+            dt += time.perf_counter() - t
+    return {"value": round(rows / dt, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"records 0..{n_records - 1}, {q.shape[0]} heads x {q.shape[1]} queries x 6240 keys "
+                      f"({rows} rows, {dt:.1f} s of oracle time)"}
+
+
+def copy_calibration(args):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    ms = time_it(lambda: dst.copy_(src), args.steps, args.warmup, stream)
+    return {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms": round(ms, 4),
+            "gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def run_video(args, sampled: bool):
@@ -133,7 +172,8 @@ def run_video(args, sampled: bool):
     achieved_tfs = flops / (ms_kernel * 1e-3) / 1e12
     if sampled:
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "algorithmic_bytes": nbytes}
     else:
         roof = {"bound": "mfma", "achieved": round(achieved_tfs, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved_tfs / BF16_PEAK_TFLOPS, 4), "traffic": None}
@@ -149,7 +189,7 @@ def run_video(args, sampled: bool):
         "input_gen_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_video(2 if sampled else 1, sampled)
+        out["cpu_baseline"] = cpu_baseline_video(6 if sampled else 1, sampled)
     return out
 
 
@@ -193,7 +233,9 @@ def main():
 
     B.load()
     assert torch.cuda.is_available(), "needs a GPU"
-    if args.workload == "decode":
+    if args.copy_calibration:
+        out = copy_calibration(args)
+    elif args.workload == "decode":
         out = run_decode(args)
     else:
         out = run_video(args, sampled=args.workload == "sampled")

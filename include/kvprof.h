@@ -51,7 +51,7 @@ extern "C" {
 /* Score sources of kvprof_row_stats / kvprof_attend. */
 #define KVPROF_MODE_BF16 0   /* bf16 Q and K                                                       */
 #define KVPROF_MODE_MXFP8 1  /* MXFP8 Q and K codes (from kvprof_pack_mxfp8); bf16 Q, K = reference  */
-#define KVPROF_MODE_INT4KV 2 /* packed 4-bit K/V blobs (from kvprof_pack_int4kv); kvprof_attend only  */
+#define KVPROF_MODE_INT4KV 2 /* bf16 Q against packed 4-bit K/V blobs (from kvprof_pack_int4kv)     */
 
 /* Limits of this build. */
 #define KVPROF_HEAD_DIM 128      /* row_stats / attend head dimension                               */

@@ -37,7 +37,9 @@ constexpr int NT = 4;    // selected ranks per row
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kPScale = 32768.f;  // P is fed to the f16 MFMA as p * 2^15
-constexpr int kRing = 3;  // K tiles in flight per wave (bf16 path): LDS ring filled by direct loads
+constexpr int kRing = 3;
+constexpr unsigned long long kOne = 1ull << 44;            // one key in a packed histogram counter
+constexpr unsigned long long kMassMask = (1ull << 44) - 1;  // K tiles in flight per wave (bf16 path): LDS ring filled by direct loads
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -46,20 +48,34 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Keys are ordered by (D, j): D the 32-bit order key of the score, j the key index. The group that
+// holds a target's rank is narrowed one 8-bit digit at a time, first over D (phase 0: the group is
+// {D >> sh == prefix}), then, if one value of D still holds too many keys, over j (phase 1: the
+// group is {D == dfix, j >> sh == prefix}). All of it in 32-bit arithmetic.
 struct TState {
-  unsigned long long prefix;  // key >> pos of the group holding the target
-  int pos, width;             // current digit position / width in the 48-bit key
-  int cnt_before;             // elements ranked before the group
-  int cnt_in;                 // elements in the group
-  int target;                 // 0-based rank to locate
+  unsigned prefix;        // digits fixed so far
+  unsigned dfix;          // phase 1: the order key shared by the group
+  int ph, sh;             // phase and shift of the group's digits
+  int valid;              // 0 for rows past the end of the problem
+  int cnt_before;         // elements ranked before the group
+  int cnt_in;             // elements in the group
+  int target;             // 0-based rank to locate
   int resolved;
-  unsigned mass_before;       // fixed-point (2^31 = 1) mass ranked before the group
+  unsigned mass_before;   // fixed-point (2^31 = 1) mass ranked before the group
   float frac;
 };
 
+__device__ __forceinline__ bool ts_in(unsigned D, int j, int ph, int sh, unsigned pre, unsigned dfix) {
+  return ph ? (D == dfix && ((unsigned)j >> sh) == pre) : ((D >> sh) == pre);
+}
+__device__ __forceinline__ bool ts_before(unsigned D, int j, int ph, int sh, unsigned pre, unsigned dfix) {
+  return ph ? (D < dfix || (D == dfix && ((unsigned)j >> sh) < pre)) : ((D >> sh) < pre);
+}
+
 struct Sel {
-  unsigned hcnt[ROWS][HB];
-  unsigned hmass[ROWS][HB];
+  // one 64-bit counter per bin: key count in bits 44..63, fixed-point mass (2^31 = 1) in bits 0..43,
+  // so a single LDS atomic per key updates both
+  unsigned long long hist[ROWS][HB];
   float ce[ROWS][CAP];  // candidate scores u
   int cj[ROWS][CAP];
   union {
@@ -264,14 +280,15 @@ __device__ __forceinline__ f32x4 mfma_step(u32x4 a, u32x4 b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
 }
 
-// Per-row scan of the 256-bin histogram by one wave (lane holds bins 4*lane..4*lane+3). Locates,
-// for every unresolved target of the row, the bin that holds its rank and narrows the target state.
-__device__ void scan_row(Smem& sm, int row, int lane, int level) {
+// Per-row scan of the level-1 histogram (the top 8 bits of D) by one wave (lane holds bins
+// 4*lane..4*lane+3): locates, for every target of the row, the bin that holds its rank.
+__device__ void scan_row(Smem& sm, int row, int lane) {
   unsigned c[4], m[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    c[q] = sm.u.sel.hcnt[row][4 * lane + q];
-    m[q] = sm.u.sel.hmass[row][4 * lane + q];
+    const unsigned long long h = sm.u.sel.hist[row][4 * lane + q];
+    c[q] = (unsigned)(h >> 44);
+    m[q] = (unsigned)(h & kMassMask);
   }
   unsigned lc = c[0] + c[1] + c[2] + c[3];
   unsigned lm = m[0] + m[1] + m[2] + m[3];
@@ -287,14 +304,14 @@ __device__ void scan_row(Smem& sm, int row, int lane, int level) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     TState& ts = sm.ts[row][t];
-    if (ts.resolved && level > 0) continue;
-    if (level > 0 && ts.width == 0) continue;
+    if (!ts.valid) continue;
     unsigned T = (unsigned)(ts.target - ts.cnt_before);
     unsigned r0 = run, m0 = mrun;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (r0 <= T && T < r0 + c[q]) {
-        ts.prefix = (ts.prefix << ts.width) | (unsigned long long)(4 * lane + q);
+        ts.prefix = (unsigned)(4 * lane + q);
+        ts.sh = kSh;
         ts.cnt_before += (int)r0;
         ts.mass_before += m0;
         ts.cnt_in = (int)c[q];
@@ -357,11 +374,12 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       sm.qs[r][c] = v;
     }
   }
-  for (int j = tid; j < p.n_k; j += WGT) sm.bias2[j] = p.key_bias ? p.key_bias[j] * kLog2e : 0.f;
+  // staged over the padded key range, so each lane reads its 4 bias values as one aligned 16-byte load
+  for (int j = tid; j < KVPROF_MAX_KEYS; j += WGT) sm.bias2[j] = (p.key_bias && j < p.n_k) ? p.key_bias[j] * kLog2e : 0.f;
   __syncthreads();
 
   // ---- A: scores ---------------------------------------------------------------------------------
-  const int kbase = w * TPW * 16;
+  const int kbase = __builtin_amdgcn_readfirstlane(w * TPW * 16);  // wave-uniform: keep it scalar
   float sc[TPW][4];
   float umax = -INFINITY, umin = INFINITY;
   // The scheduling barrier at the end of each tile keeps the compiler from hoisting every tile's
@@ -414,11 +432,8 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         acc = mfma_step<KSRC>(kl[ks], sm.qs[r][ks * 4 + g], acc);
       }
     }
-    float bias[4] = {0.f, 0.f, 0.f, 0.f};
-    if (p.key_bias && j0 < kmax) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bias[i] = (j0 + 4 * g + i < p.n_k) ? sm.bias2[j0 + 4 * g + i] : 0.f;
-    }
+    f32x4 bias = {0.f, 0.f, 0.f, 0.f};
+    if (p.key_bias) bias = *reinterpret_cast<const f32x4*>(&sm.bias2[j0 + 4 * g]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = j0 + 4 * g + i;
@@ -513,7 +528,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   if (g == 0) sm.red_e[w][r] = esum;
   // the histogram shares LDS with the phase-A load ring: clear it only now (every ring load has
   // completed: the last tile waited for vmcnt(0))
-  for (int i = tid; i < ROWS * HB * 2; i += WGT) (&sm.u.sel.hcnt[0][0])[i] = 0u;
+  for (int i = tid; i < ROWS * HB; i += WGT) (&sm.u.sel.hist[0][0])[i] = 0ull;
   __syncthreads();
 
   // ---- per-row finalisation of B (wave w handles rows w and w + 8) --------------------------------------------
@@ -582,8 +597,10 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         const int n = ri.nvis;
         TState ts;
         ts.prefix = 0;
-        ts.pos = 16 + kSh;
-        ts.width = 8;
+        ts.dfix = 0;
+        ts.ph = 0;
+        ts.sh = kSh;
+        ts.valid = 1;
         ts.cnt_before = 0;
         ts.cnt_in = 0;
         ts.resolved = 0;
@@ -601,7 +618,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     } else if (lane < NT) {
       TState ts{};
       ts.resolved = 1;
-      ts.width = 0;
+      ts.valid = 0;
       sm.ts[row][lane] = ts;
     }
   }
@@ -620,15 +637,14 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         const float u = sc[t][i];
         const float e = __builtin_amdgcn_exp2f(fmaxf(u + offq, -256.f));
         const int dig = (int)(dkey(u, mq, ksq) >> kSh);
-        atomicAdd(&sm.u.sel.hcnt[r][dig], 1u);
-        atomicAdd(&sm.u.sel.hmass[r][dig], (unsigned)__builtin_rintf(e * ifx));
+        atomicAdd(&sm.u.sel.hist[r][dig], kOne + (unsigned long long)__builtin_rintf(e * ifx));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   }
   __syncthreads();
-  for (int row = w; row < ROWS; row += NW) scan_row(sm, row, lane, 0);
+  for (int row = w; row < ROWS; row += NW) scan_row(sm, row, lane);
   __syncthreads();
 
   // ---- D: exact ranks ------------------------------------------------------------------------------
@@ -645,10 +661,10 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       int tot = 0, bad = 0;
       for (int t = 0; t < NT; ++t) {
         const TState& ts = sm.ts[row][t];
-        if (ts.width == 0) continue;  // invalid row
+        if (!ts.valid) continue;  // row past the end
         if (!ts.resolved) bad = 1;
         bool seen = false;
-        for (int q = 0; q < t; ++q) seen |= sm.ts[row][q].width > 0 && sm.ts[row][q].prefix == ts.prefix;
+        for (int q = 0; q < t; ++q) seen |= sm.ts[row][q].valid && sm.ts[row][q].prefix == ts.prefix;
         if (!seen) tot += ts.cnt_in;
       }
       if (bad || tot > CAP) atomicOr(&sm.flag, 1);
@@ -665,39 +681,63 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       // boundary bins of this lane's row (level-1 digits)
       int bq[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) bq[t] = sm.ts[r][t].width > 0 ? (int)sm.ts[r][t].prefix : -1;
-      const int bmax = max(max(bq[0], bq[1]), max(bq[2], bq[3]));
-      const int gq = opaque(g), nv = opaque(nvis);
-      const float mq = rc_m(), ksq = rc_ks();
+      for (int t = 0; t < NT; ++t) bq[t] = sm.ts[r][t].valid ? (int)sm.ts[r][t].prefix : -1;
+      // Two passes without returning atomics in the loop: count this lane's winners and candidates,
+      // reserve slots with one atomic each, then write.
+      int nw = 0, nc = 0;
+      {
+        const int gq = opaque(g), nv = opaque(nvis);
+        const float mq = rc_m(), ksq = rc_ks();
 #pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) {
-        const int j0 = kbase + tt * 16;
+        for (int tt = 0; tt < TPW; ++tt) {
+          const int j0 = kbase + tt * 16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = j0 + 4 * gq + i;
-          const float u = sc[tt][i];
-          const unsigned D = dkey(u, mq, ksq);
-          const int dig = (int)(D >> kSh);
-          if (j < nv && dig <= bmax) {
+          for (int i = 0; i < 4; ++i) {
+            const int dig = (int)(dkey(sc[tt][i], mq, ksq) >> kSh);
+            const bool ok = j0 + 4 * gq + i < nv;
+            nw += (ok && dig < bq[0]) ? 1 : 0;
+            nc += (ok && (dig == bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3])) ? 1 : 0;
+          }
+          nw = opaque(nw);
+          nc = opaque(nc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      int wpos = nw ? atomicAdd(&sm.nwin[r], nw) : 0;
+      int cpos = nc ? atomicAdd(&sm.ncand[r], nc) : 0;
+      if (nw | nc) {
+        const int gq = opaque(g), nv = opaque(nvis);
+        const float mq = rc_m(), ksq = rc_ks();
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+          const int j0 = kbase + tt * 16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = j0 + 4 * gq + i;
+            const float u = sc[tt][i];
+            const int dig = (int)(dkey(u, mq, ksq) >> kSh);
+            const bool ok = j < nv;
             // a key can be both: ranked above the top-32 boundary and inside the boundary bin of a
             // 1/5/10 % rank (at small n those ranks lie above rank 31)
-            if (dig < bq[0]) {
-              const int slot = atomicAdd(&sm.nwin[r], 1);
-              if (slot < 32) {
-                sm.win_u[r][slot] = u;
-                sm.win_j[r][slot] = j;
+            if (ok && dig < bq[0]) {
+              if (wpos < 32) {
+                sm.win_u[r][wpos] = u;
+                sm.win_j[r][wpos] = j;
               }
+              ++wpos;
             }
-            if (dig == bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3]) {
-              const int slot = atomicAdd(&sm.ncand[r], 1);
-              if (slot < CAP) {
-                sm.u.sel.ce[r][slot] = u;
-                sm.u.sel.cj[r][slot] = j;
+            if (ok && (dig == bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3])) {
+              if (cpos < CAP) {
+                sm.u.sel.ce[r][cpos] = u;
+                sm.u.sel.cj[r][cpos] = j;
               }
+              ++cpos;
             }
           }
+          wpos = opaque(wpos);
+          cpos = opaque(cpos);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();
@@ -732,7 +772,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const TState& ts = sm.ts[row][t];
-          if (ts.width == 0 || (unsigned)ts.prefix != dga) continue;
+          if (!ts.valid || ts.prefix != dga) continue;
           const int rr = ts.target - ts.cnt_before;
           if (t == 0) {
             if (rk <= rr) {  // ranks 0..target of the top-32 list
@@ -762,20 +802,15 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       if (tid == 0) sm.flag = 0;
       __syncthreads();
       for (int row = w; row < ROWS; row += NW)
-        if (lane == 0 && !sm.ts[row][t].resolved && sm.ts[row][t].width > 0) atomicOr(&sm.flag, 1);
+        if (lane == 0 && !sm.ts[row][t].resolved && sm.ts[row][t].valid) atomicOr(&sm.flag, 1);
       __syncthreads();
       if (!sm.flag) break;
-      // next digit of the 48-bit key (D << 16 | j)
-      const TState tsr = sm.ts[r][t];
-      const bool active_row = !tsr.resolved && tsr.width > 0;
-      int npos = tsr.pos - 8, nwid = 8;
-      if (npos < 0) {
-        nwid = tsr.pos;
-        npos = 0;
-      }
-      for (int i = tid; i < ROWS * HB * 2; i += WGT) (&sm.u.sel.hcnt[0][0])[i] = 0u;
+      for (int i = tid; i < ROWS * HB; i += WGT) (&sm.u.sel.hist[0][0])[i] = 0ull;
       __syncthreads();
-      if (active_row) {
+      // histogram of the next 8-bit digit over the group of every unresolved target
+      if (!sm.ts[r][t].resolved && sm.ts[r][t].valid) {
+        const int ph = opaque(sm.ts[r][t].ph), sh = opaque(sm.ts[r][t].sh);
+        const unsigned pre = opaque(sm.ts[r][t].prefix), dfix = opaque(sm.ts[r][t].dfix);
         const int gq = opaque(g), nv = opaque(nvis);
         const float mq = rc_m(), ksq = rc_ks(), offq = 64.f - mq;
         const float ifx = rc_fx();
@@ -788,12 +823,10 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
             if (j < nv) {
               const float u = sc[tt][i];
               const unsigned D = dkey(u, mq, ksq);
-              const unsigned long long key = ((unsigned long long)D << 16) | (unsigned)j;
-              if ((key >> (npos + nwid)) == tsr.prefix) {
-                const int dig = (int)((key >> npos) & ((1ull << nwid) - 1));
+              if (ts_in(D, j, ph, sh, pre, dfix)) {
+                const int dig = (int)(((ph ? (unsigned)j : D) >> (sh - 8)) & 255u);
                 const float e = __builtin_amdgcn_exp2f(fmaxf(u + offq, -256.f));
-                atomicAdd(&sm.u.sel.hcnt[r][dig], 1u);
-                atomicAdd(&sm.u.sel.hmass[r][dig], (unsigned)__builtin_rintf(e * ifx));
+                atomicAdd(&sm.u.sel.hist[r][dig], kOne + (unsigned long long)__builtin_rintf(e * ifx));
               }
             }
           }
@@ -803,17 +836,13 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       __syncthreads();
       for (int row = w; row < ROWS; row += NW) {
         const TState ts = sm.ts[row][t];
-        const bool act = !ts.resolved && ts.width > 0;
-        int wpos = ts.pos - 8, wwid = 8;
-        if (wpos < 0) {
-          wwid = ts.pos;
-          wpos = 0;
-        }
+        const bool act = !ts.resolved && ts.valid;
         unsigned c[4], mm[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          c[q] = sm.u.sel.hcnt[row][4 * lane + q];
-          mm[q] = sm.u.sel.hmass[row][4 * lane + q];
+          const unsigned long long h = sm.u.sel.hist[row][4 * lane + q];
+          c[q] = (unsigned)(h >> 44);
+          mm[q] = (unsigned)(h & kMassMask);
         }
         unsigned lc = c[0] + c[1] + c[2] + c[3], lm = mm[0] + mm[1] + mm[2] + mm[3];
         unsigned ic = lc, im = lm;
@@ -832,13 +861,19 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         for (int q = 0; q < 4; ++q) {
           if (r0 <= T && T < r0 + c[q]) {
             found = true;
-            nt.prefix = (ts.prefix << wwid) | (unsigned long long)(4 * lane + q);
+            nt.prefix = (ts.prefix << 8) | (unsigned)(4 * lane + q);
+            nt.sh = ts.sh - 8;
             nt.cnt_before = ts.cnt_before + (int)r0;
             nt.mass_before = ts.mass_before + m0;
             nt.cnt_in = (int)c[q];
-            nt.pos = wpos;
-            nt.width = wwid;
-            nt.resolved = c[q] <= (unsigned)CAP || wpos == 0;
+            nt.resolved = c[q] <= (unsigned)CAP || (ts.ph == 1 && nt.sh == 0);
+            if (!nt.resolved && ts.ph == 0 && nt.sh == 0) {
+              // more than CAP keys share one order key: continue on their indices (j < 2^16)
+              nt.ph = 1;
+              nt.dfix = nt.prefix;
+              nt.prefix = 0;
+              nt.sh = 16;
+            }
           }
           r0 += c[q];
           m0 += mm[q];
@@ -855,40 +890,36 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       if (t == 0) sm.nwin[tid] = 0;
     }
     __syncthreads();
-    {
-      const TState tsr = sm.ts[r][t];
-      const bool rowok = nvis > 0 && tsr.width > 0;
-      if (rowok) {
-        const int gq = opaque(g), nv = opaque(nvis);
-        const float mq = rc_m(), ksq = rc_ks();
+    if (nvis > 0 && sm.ts[r][t].valid) {
+      const int ph = opaque(sm.ts[r][t].ph), sh = opaque(sm.ts[r][t].sh);
+      const unsigned pre = opaque(sm.ts[r][t].prefix), dfix = opaque(sm.ts[r][t].dfix);
+      const int gq = opaque(g), nv = opaque(nvis);
+      const float mq = rc_m(), ksq = rc_ks();
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-          const int j0 = kbase + tt * 16;
+      for (int tt = 0; tt < TPW; ++tt) {
+        const int j0 = kbase + tt * 16;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = j0 + 4 * gq + i;
-            if (j < nv) {
-              const float u = sc[tt][i];
-              const unsigned D = dkey(u, mq, ksq);
-              const unsigned long long key = ((unsigned long long)D << 16) | (unsigned)j;
-              const unsigned long long kp = key >> tsr.pos;
-              if (kp == tsr.prefix) {
-                const int slot = atomicAdd(&sm.ncand[r], 1);
-                if (slot < CAP) {
-                  sm.u.sel.ce[r][slot] = u;
-                  sm.u.sel.cj[r][slot] = j;
-                }
-              } else if (t == 0 && kp < tsr.prefix) {
-                const int slot = atomicAdd(&sm.nwin[r], 1);
-                if (slot < 32) {
-                  sm.win_u[r][slot] = u;
-                  sm.win_j[r][slot] = j;
-                }
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + 4 * gq + i;
+          if (j < nv) {
+            const float u = sc[tt][i];
+            const unsigned D = dkey(u, mq, ksq);
+            if (ts_in(D, j, ph, sh, pre, dfix)) {
+              const int slot = atomicAdd(&sm.ncand[r], 1);
+              if (slot < CAP) {
+                sm.u.sel.ce[r][slot] = u;
+                sm.u.sel.cj[r][slot] = j;
+              }
+            } else if (t == 0 && ts_before(D, j, ph, sh, pre, dfix)) {
+              const int slot = atomicAdd(&sm.nwin[r], 1);
+              if (slot < 32) {
+                sm.win_u[r][slot] = u;
+                sm.win_j[r][slot] = j;
               }
             }
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();
@@ -897,7 +928,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       const TState ts = sm.ts[row][t];
       const int c = min(sm.ncand[row], CAP);
       const float mr = sm.r_m[row], ksr = row_ks(row);
-      if (ts.width > 0) {
+      if (ts.valid) {
         for (int a = lane; a < c; a += 64) {
           const float ua = sm.u.sel.ce[row][a];
           const int ja = sm.u.sel.cj[row][a];
@@ -924,7 +955,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     if (t > 0) for (int row = w; row < ROWS; row += NW) {
       const TState ts = sm.ts[row][t];
       const RowInfo ri = row_info(p, b, hkv, rb, row);
-      if (ri.ok && ts.width > 0) {
+      if (ri.ok && ts.valid) {
         const int rr = ts.target - ts.cnt_before;
         const int c = min(sm.ncand[row], CAP);
         float a = 0.f;
