@@ -39,7 +39,9 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kPScale = 32768.f;  // P is fed to the f16 MFMA as p * 2^15
 constexpr int kRing = 3;
 constexpr unsigned long long kOne = 1ull << 44;            // one key in a packed histogram counter
-constexpr unsigned long long kMassMask = (1ull << 44) - 1;  // K tiles in flight per wave (bf16 path): LDS ring filled by direct loads
+constexpr unsigned long long kMassMask = (1ull << 44) - 1;
+constexpr float kNegBig = -3.0e38f;  // floor of a visible key's score
+constexpr float kSelSigma = 0.8f;    // selection threshold: mean + kSelSigma * standard deviation
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -61,7 +63,7 @@ struct TState {
   int cnt_in;             // elements in the group
   int target;             // 0-based rank to locate
   int resolved;
-  unsigned mass_before;   // fixed-point (2^31 = 1) mass ranked before the group
+  unsigned long long mass_before;  // fixed-point mass (units of 2^33 / Z') ranked before the group
   float frac;
 };
 
@@ -89,10 +91,13 @@ struct Smem {
   float red_b[NW][ROWS];
   float red_e[NW][ROWS];
   int red_i[NW][ROWS];
+  float red_c[NW][ROWS];
+  float red_d[NW][ROWS];
   float segpart[NW][ROWS][kSegPerWave];
   float segmass[ROWS][kMaxSeg];
   int cs0[NW];
-  float r_z[ROWS], r_e[ROWS], r_m[ROWS], r_mn[ROWS];
+  float r_z[ROWS], r_e[ROWS], r_m[ROWS], r_mn[ROWS], r_T[ROWS], r_k8[ROWS];
+  int rfb[ROWS];  // 1: the row's histogram is redone over every visible key
   int flag;
   TState ts[ROWS][NT];
   float tmass[ROWS][3];
@@ -100,7 +105,7 @@ struct Smem {
   float win_u[ROWS][32];  // scores of the top-32 keys
   int win_j[ROWS][32];
   int top0[ROWS];
-  u32x4 qs[ROWS][16];  // Q rows as 16-byte chunks (B operand of S^T = K Q^T)
+  u32x4 qs[ROWS][17];  // Q rows as 16-byte chunks (B operand of S^T = K Q^T); padded against bank conflicts
   float bias2[KVPROF_MAX_KEYS];  // key bias * log2(e)
   union {
     Sel sel;
@@ -167,13 +172,24 @@ __device__ __forceinline__ T opaque(T x) {
   return x;
 }
 
-// 32-bit order key of a score u inside its row: (max - u) scaled so that the row's range [min, max]
-// spans [0, 2^32). Monotone (a larger score never gets a larger key) and free of underflow, unlike
-// probabilities; explicit rounding intrinsics make every pass compute the identical key.
-__device__ __forceinline__ unsigned dkey(float u, float m, float kscale) {
-  return (unsigned)fminf(__fmul_rn(__fsub_rn(m, u), kscale), 4294967040.f);
+// Level-1 bin of a score at or above the row's selection threshold T: 256 equal bins over
+// [T, max], bin 0 holding the largest scores. Monotone (a larger score never gets a larger bin);
+// explicit rounding intrinsics make every pass compute the identical bin.
+__device__ __forceinline__ float bin_scale(float m, float T) {
+  const float d = m - T;
+  return (d > 1e-20f && d < 1e30f) ? 256.f / d : 0.f;  // 0: every key in bin 0 (ranked by index)
 }
-constexpr int kSh = 24;  // level-1 digit = key >> 24 (256 equal bins over the row's score range)
+__device__ __forceinline__ int bin1(float u, float m, float k8) {
+  return (int)fminf(__fmul_rn(__fsub_rn(m, u), k8), 255.f);
+}
+// 32-bit order key for the refinement levels: the same quantity scaled by 2^24 (an exact power of
+// two, so key >> 24 is the level-1 bin).
+__device__ __forceinline__ unsigned dkey32(float u, float m, float k32) {
+  return (unsigned)fminf(__fmul_rn(__fsub_rn(m, u), k32), 4294967040.f);
+}
+// Fixed-point mass of a key with e' = 2^(u - max + 64): round(e' 2^-33) <= 2^31.
+__device__ __forceinline__ unsigned fixmass(float e) { return (unsigned)fmaf(e, 0x1p-33f, 0.5f); }
+constexpr int kSh = 24;  // level-1 bin = key >> 24
 
 __device__ __forceinline__ int remap_block(int bid, int n) {
   // Dispatch places consecutive workgroups on the 8 XCDs round-robin; this mapping gives each XCD a
@@ -280,33 +296,62 @@ __device__ __forceinline__ f32x4 mfma_step(u32x4 a, u32x4 b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
 }
 
-// Per-row scan of the level-1 histogram (the top 8 bits of D) by one wave (lane holds bins
-// 4*lane..4*lane+3): locates, for every target of the row, the bin that holds its rank.
+__device__ __forceinline__ void init_target(TState& ts, int t, int n) {
+  ts.prefix = 0;
+  ts.dfix = 0;
+  ts.ph = 0;
+  ts.sh = kSh;
+  ts.valid = n > 0;
+  ts.cnt_before = 0;
+  ts.cnt_in = 0;
+  ts.resolved = n > 0 ? 0 : 1;
+  ts.mass_before = 0;
+  if (t == 0) {
+    ts.target = min(31, n - 1);
+    ts.frac = 0.f;
+  } else {
+    const int pct = t == 1 ? 1 : (t == 2 ? 5 : 10);
+    ts.target = (n * pct) / 100;
+    ts.frac = (float)((n * pct) % 100) / 100.f;
+  }
+}
+
+// Per-row scan of the level-1 histogram by one wave (lane holds bins 4*lane..4*lane+3): locates, for
+// every target of the row, the bin that holds its rank. A row whose histogram holds no more keys than
+// its deepest target is marked for a redo over every visible key.
 __device__ void scan_row(Smem& sm, int row, int lane) {
-  unsigned c[4], m[4];
+  unsigned c[4];
+  unsigned long long m[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const unsigned long long h = sm.u.sel.hist[row][4 * lane + q];
     c[q] = (unsigned)(h >> 44);
-    m[q] = (unsigned)(h & kMassMask);
+    m[q] = h & kMassMask;
   }
-  unsigned lc = c[0] + c[1] + c[2] + c[3];
-  unsigned lm = m[0] + m[1] + m[2] + m[3];
-  unsigned ic = lc, im = lm;
+  const unsigned lc = c[0] + c[1] + c[2] + c[3];
+  const unsigned long long lm = m[0] + m[1] + m[2] + m[3];
+  unsigned ic = lc;
+  unsigned long long im = lm;
   for (int o = 1; o < 64; o <<= 1) {
-    unsigned tc = __shfl_up(ic, o), tm = __shfl_up(im, o);
+    const unsigned tc = __shfl_up(ic, o);
+    const unsigned long long tm = __shfl_up(im, o);
     if (lane >= o) {
       ic += tc;
       im += tm;
     }
   }
-  unsigned run = ic - lc, mrun = im - lm;
+  const unsigned total = __shfl(ic, 63);
+  const unsigned run = ic - lc;
+  const unsigned long long mrun = im - lm;
+  int redo = 0;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     TState& ts = sm.ts[row][t];
     if (!ts.valid) continue;
-    unsigned T = (unsigned)(ts.target - ts.cnt_before);
-    unsigned r0 = run, m0 = mrun;
+    const unsigned T = (unsigned)(ts.target - ts.cnt_before);
+    redo |= T >= total;
+    unsigned r0 = run;
+    unsigned long long m0 = mrun;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (r0 <= T && T < r0 + c[q]) {
@@ -320,6 +365,10 @@ __device__ void scan_row(Smem& sm, int row, int lane) {
       r0 += c[q];
       m0 += m[q];
     }
+  }
+  if (lane == 0) {
+    sm.rfb[row] = redo;
+    if (redo) atomicOr(&sm.flag, 1);
   }
 }
 
@@ -381,7 +430,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   // ---- A: scores ---------------------------------------------------------------------------------
   const int kbase = __builtin_amdgcn_readfirstlane(w * TPW * 16);  // wave-uniform: keep it scalar
   float sc[TPW][4];
-  float umax = -INFINITY, umin = INFINITY;
+  float umax = -INFINITY, umin = INFINITY, usum = 0.f, usq = 0.f;
   // The scheduling barrier at the end of each tile keeps the compiler from hoisting every tile's
   // loads, which would push the score registers out to scratch.
   if (KSRC == KSRC_BF16) {
@@ -437,24 +486,34 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = j0 + 4 * g + i;
-      float u = fmaf(acc[i], p.scale_log2, bias[i]);
       const bool valid = j < nvis;
-      u = valid ? u : -INFINITY;
+      // visible keys are clamped to a finite floor (a -inf bias or a NaN becomes a zero probability);
+      // invisible keys are -inf, so they never pass a selection threshold
+      const float u = valid ? fmaxf(fmaf(acc[i], p.scale_log2, bias[i]), kNegBig) : -INFINITY;
       // pinned here: otherwise the compiler sinks this epilogue to the next use and keeps both the
       // MFMA accumulators and the bias values live for every tile
       sc[t][i] = opaque(u);
+      const float uv = valid ? u : 0.f;
       umax = fmaxf(umax, u);
       umin = valid ? fminf(umin, u) : umin;
+      usum += uv;
+      usq = fmaf(uv, uv, usq);
     }
     umax = opaque(umax);
     umin = opaque(umin);
+    usum = opaque(usum);
+    usq = opaque(usq);
     __builtin_amdgcn_sched_barrier(0);
   }
   umax = row_max4(umax);
   umin = row_min4(umin);
+  usum = row_sum4(usum);
+  usq = row_sum4(usq);
   if (g == 0) {
     sm.red_a[w][r] = umax;
     sm.red_b[w][r] = umin;
+    sm.red_c[w][r] = usum;
+    sm.red_d[w][r] = usq;
   }
   // first segment overlapping this wave's keys
   int cs = 0;
@@ -462,26 +521,48 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   const int cs_first = cs;
   if (lane == 0) sm.cs0[w] = cs_first;
   __syncthreads();
-  float m = -INFINITY, mn = INFINITY;
+  float m = -INFINITY, mn = INFINITY, s1 = 0.f, s2 = 0.f;
 #pragma unroll
   for (int ww = 0; ww < NW; ++ww) {
     m = fmaxf(m, sm.red_a[ww][r]);
     mn = fminf(mn, sm.red_b[ww][r]);
+    s1 += sm.red_c[ww][r];
+    s2 += sm.red_d[ww][r];
   }
-  if (!me0.ok) {
+  // Selection threshold: only keys at or above T enter the level-1 histogram. T sits kSelSigma
+  // standard deviations above the row mean, which keeps a few times more keys than the deepest rank
+  // (10 %) needs for bell-shaped rows; a row whose histogram ends up too small is redone with T = min.
+  float T = m;
+  if (me0.ok) {
+    const float mu = s1 / (float)nvis;
+    const float sd = sqrtf(fmaxf(s2 / (float)nvis - mu * mu, 0.f));
+    T = fmaxf(fminf(m, fmaf(kSelSigma, sd, mu)), mn);
+  } else {
     m = 0.f;
     mn = 0.f;
+    T = 0.f;
   }
+  const float k8 = bin_scale(m, T);
   if (w == 0 && g == 0) {
     sm.r_m[r] = m;
     sm.r_mn[r] = mn;
+    sm.r_T[r] = T;
+    sm.r_k8[r] = k8;
   }
+  // the histogram shares LDS with the phase-A load ring, which every wave has finished reading
+  for (int i = tid; i < ROWS * HB; i += WGT) (&sm.u.sel.hist[0][0])[i] = 0ull;
+  __syncthreads();
 
-  // ---- B: exponentials, entropy sum, segment masses -----------------------------------------------
+  // ---- B: exponentials, entropy sum, segment masses and the level-1 histogram ---------------------
+  // Histogram counters pack a key count (bits 44..63) with a fixed-point mass f = round(e' 2^-33)
+  // (bits 0..43), e' = 2^(u - max + 64): f <= 2^31 per key, so a row of <= 8192 keys cannot carry
+  // out of the mass field. One LDS atomic per selected key updates both.
+  {
   const float off = 64.f - m;
   float esum = 0.f, acc_seg = 0.f;
   int nb = (cs < p.n_seg) ? p.seg_bounds[cs + 1] : 0x7fffffff;
   const int gB = opaque(g);
+  const float Tq = opaque(T), k8q = opaque(k8), mq = opaque(m);
   auto flush = [&](float a, int seg) {
     float v = row_sum4(a);
     if (g == 0 && seg - cs_first < kSegPerWave) sm.segpart[w][r][seg - cs_first] = v;
@@ -493,9 +574,12 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     float e[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float tp = fmaxf(sc[t][i] + off, -256.f);
+      const float u = sc[t][i];
+      const float tp = fmaxf(u + off, -256.f);
       e[i] = __builtin_amdgcn_exp2f(tp);
       esum = fmaf(e[i], tp, esum);
+      if (u >= Tq)
+        atomicAdd(&sm.u.sel.hist[r][bin1(u, mq, k8q)], kOne + (unsigned long long)fixmass(e[i]));
     }
     if (j0 + 16 <= nb) {
       acc_seg += (e[0] + e[1]) + (e[2] + e[3]);
@@ -526,9 +610,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   if (kbase < kmax && cs < p.n_seg) flush(acc_seg, cs);
   esum = row_sum4(esum);
   if (g == 0) sm.red_e[w][r] = esum;
-  // the histogram shares LDS with the phase-A load ring: clear it only now (every ring load has
-  // completed: the last tile waited for vmcnt(0))
-  for (int i = tid; i < ROWS * HB; i += WGT) (&sm.u.sel.hist[0][0])[i] = 0ull;
+  }
   __syncthreads();
 
   // ---- per-row finalisation of B (wave w handles rows w and w + 8) --------------------------------------------
@@ -537,10 +619,10 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     const int span = TPW * 16;
     for (int s = lane; s < p.n_seg; s += 64) {
       float v = 0.f;
-      const int s0 = p.seg_bounds[s], s1 = p.seg_bounds[s + 1];
+      const int s0 = p.seg_bounds[s], s1_ = p.seg_bounds[s + 1];
       for (int ww = 0; ww < NW; ++ww) {
         const int w0 = ww * span, w1 = w0 + span;
-        if (w0 < s1 && w1 > s0) {
+        if (w0 < s1_ && w1 > s0) {
           const int slot = s - sm.cs0[ww];
           if (slot >= 0 && slot < kSegPerWave) v += sm.segpart[ww][row][slot];
         }
@@ -563,17 +645,10 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   // registers next to the scores for the rest of the kernel).
   auto rc_m = [&]() { return sm.r_m[r]; };
   auto rc_z = [&]() { return sm.r_z[r]; };
-  auto rc_ks = [&]() {
-    const float d = sm.r_m[r] - sm.r_mn[r];
-    return d > 0.f ? 4294967040.f / d : 0.f;
-  };
-  auto rc_fx = [&]() { return 2147483648.f / sm.r_z[r]; };
+  auto rc_T = [&]() { return sm.r_T[r]; };
+  auto rc_k8 = [&]() { return sm.r_k8[r]; };
   // p <= 2^-150 (an fp32 zero) <=> u - max + 64 - log2 Z' <= -150
   auto rc_thr = [&]() { return sm.r_m[r] + log2f(sm.r_z[r]) - 214.f; };
-  auto row_ks = [&](int row) {
-    const float d = sm.r_m[row] - sm.r_mn[row];
-    return d > 0.f ? 4294967040.f / d : 0.f;
-  };
 
   // region / frame / scalar outputs and target setup (wave w handles rows w and w + 8)
   for (int row = w; row < ROWS; row += NW) {
@@ -593,67 +668,55 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           if (p.seg_frame[s] == f) a += sm.segmass[row][s];
         if (p.frame_mass) p.frame_mass[ri.grow * p.n_frames + f] = a * iz;
       }
-      if (lane < NT) {
-        const int n = ri.nvis;
-        TState ts;
-        ts.prefix = 0;
-        ts.dfix = 0;
-        ts.ph = 0;
-        ts.sh = kSh;
-        ts.valid = 1;
-        ts.cnt_before = 0;
-        ts.cnt_in = 0;
-        ts.resolved = 0;
-        ts.mass_before = 0;
-        if (lane == 0) {
-          ts.target = min(31, n - 1);
-          ts.frac = 0.f;
-        } else {
-          const int pct = lane == 1 ? 1 : (lane == 2 ? 5 : 10);
-          ts.target = (n * pct) / 100;
-          ts.frac = (float)((n * pct) % 100) / 100.f;
-        }
-        sm.ts[row][lane] = ts;
-      }
-    } else if (lane < NT) {
-      TState ts{};
-      ts.resolved = 1;
-      ts.valid = 0;
-      sm.ts[row][lane] = ts;
     }
+    if (lane < NT) init_target(sm.ts[row][lane], lane, ri.ok ? ri.nvis : 0);
   }
-
-  // ---- C: level-1 histogram -------------------------------------------------------------------------
-  {
-  const int gq = opaque(g), nv = opaque(nvis);
-  const float mq = rc_m(), ksq = rc_ks(), offq = 64.f - mq, ifx = rc_fx();
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int j0 = kbase + t * 16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = j0 + 4 * gq + i;
-      if (j < nv) {
-        const float u = sc[t][i];
-        const float e = __builtin_amdgcn_exp2f(fmaxf(u + offq, -256.f));
-        const int dig = (int)(dkey(u, mq, ksq) >> kSh);
-        atomicAdd(&sm.u.sel.hist[r][dig], kOne + (unsigned long long)__builtin_rintf(e * ifx));
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  }
+  if (tid == 0) sm.flag = 0;
   __syncthreads();
   for (int row = w; row < ROWS; row += NW) scan_row(sm, row, lane);
   __syncthreads();
+
+  // Rows whose histogram holds no more keys than their deepest rank: redo it over every visible key.
+  if (sm.flag) {
+    for (int row = w; row < ROWS; row += NW) {
+      if (sm.rfb[row]) {
+        for (int i = lane; i < HB; i += 64) sm.u.sel.hist[row][i] = 0ull;
+        if (lane == 0) {
+          sm.r_T[row] = sm.r_mn[row];
+          sm.r_k8[row] = bin_scale(sm.r_m[row], sm.r_mn[row]);
+        }
+        if (lane < NT) init_target(sm.ts[row][lane], lane, row_info(p, b, hkv, rb, row).nvis);
+      }
+    }
+    __syncthreads();
+    if (sm.rfb[r]) {
+      const float mq = rc_m(), Tq = rc_T(), k8q = rc_k8(), offq = 64.f - mq;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float u = sc[t][i];
+          if (u >= Tq) {
+            const float e = __builtin_amdgcn_exp2f(fmaxf(u + offq, -256.f));
+            atomicAdd(&sm.u.sel.hist[r][bin1(u, mq, k8q)], kOne + (unsigned long long)fixmass(e));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+    for (int row = w; row < ROWS; row += NW)
+      if (sm.rfb[row]) scan_row(sm, row, lane);
+    __syncthreads();
+  }
 
   // ---- D: exact ranks ------------------------------------------------------------------------------
   // Fast path (the common case): every target's boundary bin holds at most CAP keys and the distinct
   // boundary bins of a row hold at most CAP keys together. One pass then gathers, for every row, the
   // keys of its boundary bins (candidates) and the keys ranked above the top-32 boundary (winners);
-  // candidates are ranked inside their bin by (key, index). Masses are summed as fixed-point integers,
-  // whose sum does not depend on the order. Otherwise the slow path narrows each target with further
-  // radix levels.
+  // candidates are ranked inside their bin by (score descending, index ascending). Masses are summed
+  // as fixed-point integers, whose sum does not depend on the order. Otherwise the slow path narrows
+  // each target with further radix levels.
   if (tid == 0) sm.flag = 0;
   __syncthreads();
   for (int row = w; row < ROWS; row += NW) {
@@ -678,7 +741,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   const bool slow_path = sm.flag != 0;
   if (!slow_path) {
     {
-      // boundary bins of this lane's row (level-1 digits)
+      // boundary bins of this lane's row (level-1 bins; bin1 returns 256 below the threshold)
       int bq[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) bq[t] = sm.ts[r][t].valid ? (int)sm.ts[r][t].prefix : -1;
@@ -686,17 +749,15 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       // reserve slots with one atomic each, then write.
       int nw = 0, nc = 0;
       {
-        const int gq = opaque(g), nv = opaque(nvis);
-        const float mq = rc_m(), ksq = rc_ks();
+        const float mq = rc_m(), Tq = rc_T(), k8q = rc_k8();
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
-          const int j0 = kbase + tt * 16;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int dig = (int)(dkey(sc[tt][i], mq, ksq) >> kSh);
-            const bool ok = j0 + 4 * gq + i < nv;
-            nw += (ok && dig < bq[0]) ? 1 : 0;
-            nc += (ok && (dig == bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3])) ? 1 : 0;
+            const float u = sc[tt][i];
+            const int dig = u >= Tq ? bin1(u, mq, k8q) : 256;
+            nw += dig < bq[0] ? 1 : 0;
+            nc += (dig == bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3]) ? 1 : 0;
           }
           nw = opaque(nw);
           nc = opaque(nc);
@@ -706,8 +767,8 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       int wpos = nw ? atomicAdd(&sm.nwin[r], nw) : 0;
       int cpos = nc ? atomicAdd(&sm.ncand[r], nc) : 0;
       if (nw | nc) {
-        const int gq = opaque(g), nv = opaque(nvis);
-        const float mq = rc_m(), ksq = rc_ks();
+        const int gq = opaque(g);
+        const float mq = rc_m(), Tq = rc_T(), k8q = rc_k8();
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const int j0 = kbase + tt * 16;
@@ -715,21 +776,20 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           for (int i = 0; i < 4; ++i) {
             const int j = j0 + 4 * gq + i;
             const float u = sc[tt][i];
-            const int dig = (int)(dkey(u, mq, ksq) >> kSh);
-            const bool ok = j < nv;
+            const int dig = u >= Tq ? bin1(u, mq, k8q) : 256;
             // a key can be both: ranked above the top-32 boundary and inside the boundary bin of a
             // 1/5/10 % rank (at small n those ranks lie above rank 31)
-            if (ok && dig < bq[0]) {
+            if (dig < bq[0]) {
               if (wpos < 32) {
                 sm.win_u[r][wpos] = u;
                 sm.win_j[r][wpos] = j;
               }
               ++wpos;
             }
-            if (ok && (dig == bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3])) {
+            if (dig == bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3]) {
               if (cpos < CAP) {
                 sm.u.sel.ce[r][cpos] = u;
-                sm.u.sel.cj[r][cpos] = j;
+                sm.u.sel.cj[r][cpos] = j | (dig << 16);  // bin kept beside the index (j < 2^16)
               }
               ++cpos;
             }
@@ -743,30 +803,29 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     __syncthreads();
     // rank every candidate inside its bin
     for (int row = w; row < ROWS; row += NW) {
-      const float mr = sm.r_m[row], ksr = row_ks(row);
       const int c = min(sm.ncand[row], CAP);
       for (int a = lane; a < c; a += 64) {
-        const unsigned Da = dkey(sm.u.sel.ce[row][a], mr, ksr);
-        const int ja = sm.u.sel.cj[row][a];
-        const unsigned dga = Da >> kSh;
+        const float ua = sm.u.sel.ce[row][a];
+        const int ca = sm.u.sel.cj[row][a];
         int rank = 0;
         for (int q = 0; q < c; ++q) {
-          const unsigned Dq = dkey(sm.u.sel.ce[row][q], mr, ksr);
-          const int jq = sm.u.sel.cj[row][q];
-          rank += ((Dq >> kSh) == dga) && ((Dq < Da) || (Dq == Da && jq < ja));
+          const float uq = sm.u.sel.ce[row][q];
+          const int cq = sm.u.sel.cj[row][q];
+          rank += ((cq >> 16) == (ca >> 16)) && ((uq > ua) || (uq == ua && cq < ca));
         }
         sm.u.sel.crank[row][a] = rank;
       }
     }
     __syncthreads();
     for (int row = w; row < ROWS; row += NW) {
-      const float mr = sm.r_m[row], ksr = row_ks(row), ifx = 2147483648.f / sm.r_z[row];
+      const float mr = sm.r_m[row];
       const RowInfo ri = row_info(p, b, hkv, rb, row);
       const int c = min(sm.ncand[row], CAP);
-      unsigned acc[NT] = {0u, 0u, 0u, 0u};
+      unsigned long long acc[NT] = {0ull, 0ull, 0ull, 0ull};
       for (int a = lane; a < c; a += 64) {
         const float ua = sm.u.sel.ce[row][a];
-        const unsigned dga = dkey(ua, mr, ksr) >> kSh;
+        const int ca = sm.u.sel.cj[row][a];
+        const unsigned dga = (unsigned)(ca >> 16);
         const int rk = sm.u.sel.crank[row][a];
         const float ea = __builtin_amdgcn_exp2f(fmaxf(ua + (64.f - mr), -256.f));
 #pragma unroll
@@ -777,19 +836,20 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           if (t == 0) {
             if (rk <= rr) {  // ranks 0..target of the top-32 list
               sm.win_u[row][ts.cnt_before + rk] = ua;
-              sm.win_j[row][ts.cnt_before + rk] = sm.u.sel.cj[row][a];
+              sm.win_j[row][ts.cnt_before + rk] = ca & 0xFFFF;
             }
           } else {
-            if (rk < rr) acc[t] += (unsigned)__builtin_rintf(ea * ifx);
-            if (rk == rr) acc[t] += (unsigned)__builtin_rintf(ts.frac * ea * ifx);
+            if (rk < rr) acc[t] += fixmass(ea);
+            if (rk == rr) acc[t] += fixmass(ts.frac * ea);
           }
         }
       }
 #pragma unroll
       for (int t = 1; t < NT; ++t) {
-        unsigned x = acc[t];
+        unsigned long long x = acc[t];
         for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-        if (lane == 0 && ri.ok) sm.tmass[row][t - 1] = (float)(sm.ts[row][t].mass_before + x) * 0x1p-31f;
+        if (lane == 0 && ri.ok)
+          sm.tmass[row][t - 1] = (float)(sm.ts[row][t].mass_before + x) * (0x1p33f / sm.r_z[row]);
       }
     }
     __syncthreads();
@@ -811,22 +871,21 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       if (!sm.ts[r][t].resolved && sm.ts[r][t].valid) {
         const int ph = opaque(sm.ts[r][t].ph), sh = opaque(sm.ts[r][t].sh);
         const unsigned pre = opaque(sm.ts[r][t].prefix), dfix = opaque(sm.ts[r][t].dfix);
-        const int gq = opaque(g), nv = opaque(nvis);
-        const float mq = rc_m(), ksq = rc_ks(), offq = 64.f - mq;
-        const float ifx = rc_fx();
+        const int gq = opaque(g);
+        const float mq = rc_m(), Tq = rc_T(), k32 = rc_k8() * 0x1p24f, offq = 64.f - mq;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const int j0 = kbase + tt * 16;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int j = j0 + 4 * gq + i;
-            if (j < nv) {
-              const float u = sc[tt][i];
-              const unsigned D = dkey(u, mq, ksq);
+            const float u = sc[tt][i];
+            if (u >= Tq) {
+              const unsigned D = dkey32(u, mq, k32);
               if (ts_in(D, j, ph, sh, pre, dfix)) {
                 const int dig = (int)(((ph ? (unsigned)j : D) >> (sh - 8)) & 255u);
                 const float e = __builtin_amdgcn_exp2f(fmaxf(u + offq, -256.f));
-                atomicAdd(&sm.u.sel.hist[r][dig], kOne + (unsigned long long)__builtin_rintf(e * ifx));
+                atomicAdd(&sm.u.sel.hist[r][dig], kOne + (unsigned long long)fixmass(e));
               }
             }
           }
@@ -837,23 +896,28 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       for (int row = w; row < ROWS; row += NW) {
         const TState ts = sm.ts[row][t];
         const bool act = !ts.resolved && ts.valid;
-        unsigned c[4], mm[4];
+        unsigned c[4];
+        unsigned long long mm[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const unsigned long long h = sm.u.sel.hist[row][4 * lane + q];
           c[q] = (unsigned)(h >> 44);
-          mm[q] = (unsigned)(h & kMassMask);
+          mm[q] = h & kMassMask;
         }
-        unsigned lc = c[0] + c[1] + c[2] + c[3], lm = mm[0] + mm[1] + mm[2] + mm[3];
-        unsigned ic = lc, im = lm;
+        const unsigned lc = c[0] + c[1] + c[2] + c[3];
+        const unsigned long long lm = mm[0] + mm[1] + mm[2] + mm[3];
+        unsigned ic = lc;
+        unsigned long long im = lm;
         for (int o = 1; o < 64; o <<= 1) {
-          unsigned tc = __shfl_up(ic, o), tm = __shfl_up(im, o);
+          const unsigned tc = __shfl_up(ic, o);
+          const unsigned long long tm = __shfl_up(im, o);
           if (lane >= o) {
             ic += tc;
             im += tm;
           }
         }
-        unsigned r0 = ic - lc, m0 = im - lm;
+        unsigned r0 = ic - lc;
+        unsigned long long m0 = im - lm;
         const unsigned T = (unsigned)(ts.target - ts.cnt_before);
         TState nt = ts;
         bool found = false;
@@ -890,20 +954,20 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       if (t == 0) sm.nwin[tid] = 0;
     }
     __syncthreads();
-    if (nvis > 0 && sm.ts[r][t].valid) {
+    if (sm.ts[r][t].valid) {
       const int ph = opaque(sm.ts[r][t].ph), sh = opaque(sm.ts[r][t].sh);
       const unsigned pre = opaque(sm.ts[r][t].prefix), dfix = opaque(sm.ts[r][t].dfix);
-      const int gq = opaque(g), nv = opaque(nvis);
-      const float mq = rc_m(), ksq = rc_ks();
+      const int gq = opaque(g);
+      const float mq = rc_m(), Tq = rc_T(), k32 = rc_k8() * 0x1p24f;
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt) {
         const int j0 = kbase + tt * 16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = j0 + 4 * gq + i;
-          if (j < nv) {
-            const float u = sc[tt][i];
-            const unsigned D = dkey(u, mq, ksq);
+          const float u = sc[tt][i];
+          if (u >= Tq) {
+            const unsigned D = dkey32(u, mq, k32);
             if (ts_in(D, j, ph, sh, pre, dfix)) {
               const int slot = atomicAdd(&sm.ncand[r], 1);
               if (slot < CAP) {
@@ -923,19 +987,19 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       }
     }
     __syncthreads();
-    // rank the candidates of row w exactly by (e' descending, index ascending)
+    // rank the candidates of row w exactly by (order key, index)
     for (int row = w; row < ROWS; row += NW) {
       const TState ts = sm.ts[row][t];
       const int c = min(sm.ncand[row], CAP);
-      const float mr = sm.r_m[row], ksr = row_ks(row);
+      const float mr = sm.r_m[row], k32r = sm.r_k8[row] * 0x1p24f;
       if (ts.valid) {
         for (int a = lane; a < c; a += 64) {
           const float ua = sm.u.sel.ce[row][a];
           const int ja = sm.u.sel.cj[row][a];
-          const unsigned Da = dkey(ua, mr, ksr);
+          const unsigned Da = dkey32(ua, mr, k32r);
           int rank = 0;
           for (int q = 0; q < c; ++q) {
-            const unsigned Dq = dkey(sm.u.sel.ce[row][q], mr, ksr);
+            const unsigned Dq = dkey32(sm.u.sel.ce[row][q], mr, k32r);
             const int jq = sm.u.sel.cj[row][q];
             rank += (Dq < Da) || (Dq == Da && jq < ja);
           }
@@ -964,7 +1028,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         a = wave_sum(a);
         if (lane == 0) {
           const float iz = 1.f / sm.r_z[row];
-          float mass = (float)ts.mass_before * 0x1p-31f + a * iz;
+          float mass = (float)ts.mass_before * (0x1p33f * iz) + a * iz;
           if (rr < c) mass += ts.frac * sm.u.sel.sorted_e[row][rr] * iz;
           sm.tmass[row][t - 1] = mass;
         }
@@ -978,18 +1042,16 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   // ---- E: outputs ---------------------------------------------------------------------------------
   for (int row = w; row < ROWS; row += NW) {
     const RowInfo ri = row_info(p, b, hkv, rb, row);
-    const float mr = sm.r_m[row], ksr = row_ks(row);
     if (ri.ok) {
       const int nsel = min(32, ri.nvis);
       int rank = 0, jl = -1;
       if (lane < nsel) {
         const float ul = sm.win_u[row][lane];
         jl = sm.win_j[row][lane];
-        const unsigned Dl = dkey(ul, mr, ksr);
         for (int q = 0; q < nsel; ++q) {
-          const unsigned Dq = dkey(sm.win_u[row][q], mr, ksr);
+          const float uq = sm.win_u[row][q];
           const int jq = sm.win_j[row][q];
-          rank += (Dq < Dl) || (Dq == Dl && jq < jl);
+          rank += (uq > ul) || (uq == ul && jq < jl);
         }
         if (p.top32) p.top32[ri.grow * 32 + rank] = jl;
         if (rank == 0) sm.top0[row] = jl;
