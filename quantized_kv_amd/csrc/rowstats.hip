@@ -6,15 +6,14 @@
 // S^T = K Q^T (lane l: query row l%16, keys 4*(l/16)+i of the tile). Every statistic is then a pass
 // over registers, with cross-lane / cross-wave reductions in a fixed order (bitwise deterministic):
 //
-//   A  scores u = (scale q.k + b) log2(e) on bf16 / f16 MFMA; row max and min
-//   B  e' = 2^(u - max + 64) (the offset keeps sums and the strict-zero test in the normal float
-//      range); Z', sum e'(u - max + 64) for the entropy; per-segment masses (regions, key frames).
-//      The registers keep u: ranks are taken on scores, which never underflow.
-//   C  256-bin histogram of the order key D = (max - u) scaled to the row's score range, with counts
-//      and fixed-point masses
-//   D  exact selection of four ranks (top-32 boundary, top-1/5/10 %): boundary bins are refined by
-//      further radix levels on the 48-bit key (D, key index) until at most 256 candidates remain,
-//      which are ranked exactly in LDS
+//   A  scores u = (scale q.k + b) log2(e) on bf16 / f16 MFMA; row max, min, mean and deviation
+//   B  e' = 2^(u - max + 31); Z', sum e'(u - max + 31) for the entropy; per-segment masses (regions,
+//      key frames); and, for the keys above a selection threshold T (mean + 0.8 sd), a 256-bin
+//      histogram over [T, max] with counts and fixed-point masses round(e'). The registers keep u:
+//      ranks are taken on scores, which never underflow.
+//   D  exact selection of four ranks (top-32 boundary, top-1/5/10 %): one gather of the keys ranked
+//      above the top-32 boundary bin and of the boundary bins' keys, ranked exactly in LDS; rare
+//      overfull bins are refined by further radix levels on (order key, key index)
 //   E  outputs; optional O = P.V on f16 MFMA; MXFP8 mode adds the bf16 reference row (TV, argmax)
 //      and the per-32-key E4M3/E8M0 probability path.
 //
@@ -32,7 +31,9 @@ constexpr int NW = 8;   // waves per workgroup: 2 per SIMD, so each lane may use
 constexpr int WGT = NW * 64;
 constexpr int ROWS = 16;
 constexpr int HB = 257;  // padded histogram stride (rows land in different LDS banks)
-constexpr int CAP = 256; // candidate slots per row
+constexpr int CAP = 256; // candidate slots per row (boundary bins)
+constexpr int CAPL = CAP + 32;  // fast-path list: the boundary bins plus the keys ranked above them
+constexpr float kOff = 31.f;    // e' = 2^(u - max + kOff): the largest key weighs 2^31
 constexpr int NT = 4;    // selected ranks per row
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -40,8 +41,8 @@ constexpr float kPScale = 32768.f;  // P is fed to the f16 MFMA as p * 2^15
 constexpr int kRing = 3;
 constexpr unsigned long long kOne = 1ull << 44;            // one key in a packed histogram counter
 constexpr unsigned long long kMassMask = (1ull << 44) - 1;
-constexpr float kNegBig = -3.0e38f;  // floor of a visible key's score
-constexpr float kSelSigma = 0.8f;    // selection threshold: mean + kSelSigma * standard deviation
+constexpr float kNegBig = -1.0e37f;  // floor of the staged key bias
+constexpr float kSelSigma = 0.8f;    // selection threshold: about mean + kSelSigma standard deviations
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -63,7 +64,7 @@ struct TState {
   int cnt_in;             // elements in the group
   int target;             // 0-based rank to locate
   int resolved;
-  unsigned long long mass_before;  // fixed-point mass (units of 2^33 / Z') ranked before the group
+  unsigned long long mass_before;  // fixed-point mass (units of 1 / Z') ranked before the group
   float frac;
 };
 
@@ -78,11 +79,11 @@ struct Sel {
   // one 64-bit counter per bin: key count in bits 44..63, fixed-point mass (2^31 = 1) in bits 0..43,
   // so a single LDS atomic per key updates both
   unsigned long long hist[ROWS][HB];
-  float ce[ROWS][CAP];  // candidate scores u
-  int cj[ROWS][CAP];
+  float ce[ROWS][CAPL];  // candidate scores u
+  int cj[ROWS][CAPL];    // candidate key index (fast path: | level-1 bin << 16)
   union {
     float sorted_e[ROWS][CAP];  // slow path: candidate e' by rank
-    int crank[ROWS][CAP];       // fast path: rank of a candidate inside its level-1 bin
+    int crank[ROWS][CAPL];      // fast path: rank of a candidate inside its level-1 bin
   };
 };
 
@@ -92,7 +93,6 @@ struct Smem {
   float red_e[NW][ROWS];
   int red_i[NW][ROWS];
   float red_c[NW][ROWS];
-  float red_d[NW][ROWS];
   float segpart[NW][ROWS][kSegPerWave];
   float segmass[ROWS][kMaxSeg];
   int cs0[NW];
@@ -187,8 +187,8 @@ __device__ __forceinline__ int bin1(float u, float m, float k8) {
 __device__ __forceinline__ unsigned dkey32(float u, float m, float k32) {
   return (unsigned)fminf(__fmul_rn(__fsub_rn(m, u), k32), 4294967040.f);
 }
-// Fixed-point mass of a key with e' = 2^(u - max + 64): round(e' 2^-33) <= 2^31.
-__device__ __forceinline__ unsigned fixmass(float e) { return (unsigned)fmaf(e, 0x1p-33f, 0.5f); }
+// Fixed-point mass of a key: round(e') <= 2^31.
+__device__ __forceinline__ unsigned fixmass(float e) { return (unsigned)(e + 0.5f); }
 constexpr int kSh = 24;  // level-1 bin = key >> 24
 
 __device__ __forceinline__ int remap_block(int bid, int n) {
@@ -394,6 +394,10 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   int kmax = nvis;
   for (int o = 1; o < 16; o <<= 1) kmax = max(kmax, __shfl_xor(kmax, o));
   kmax = __builtin_amdgcn_readfirstlane(kmax);  // identical on every lane: keep it scalar
+  // keys below kmin are visible to every row of the workgroup (rows past the end do not count)
+  int kmin = me0.ok ? nvis : 0x7fffffff;
+  for (int o = 1; o < 16; o <<= 1) kmin = min(kmin, __shfl_xor(kmin, o));
+  kmin = __builtin_amdgcn_readfirstlane(kmin);
 
   const size_t kvh = (size_t)b * p.n_heads_kv + hkv;
   const size_t head_bytes = (size_t)p.n_k * KVPROF_HEAD_DIM * 2;
@@ -424,13 +428,15 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     }
   }
   // staged over the padded key range, so each lane reads its 4 bias values as one aligned 16-byte load
-  for (int j = tid; j < KVPROF_MAX_KEYS; j += WGT) sm.bias2[j] = (p.key_bias && j < p.n_k) ? p.key_bias[j] * kLog2e : 0.f;
+  // (clamped to a finite floor: a -inf bias gives a zero probability, not an infinite score)
+  for (int j = tid; j < KVPROF_MAX_KEYS; j += WGT)
+    sm.bias2[j] = (p.key_bias && j < p.n_k) ? fmaxf(p.key_bias[j] * kLog2e, kNegBig) : 0.f;
   __syncthreads();
 
   // ---- A: scores ---------------------------------------------------------------------------------
   const int kbase = __builtin_amdgcn_readfirstlane(w * TPW * 16);  // wave-uniform: keep it scalar
   float sc[TPW][4];
-  float umax = -INFINITY, umin = INFINITY, usum = 0.f, usq = 0.f;
+  float umax = -INFINITY, umin = INFINITY, usum = 0.f;
   // The scheduling barrier at the end of each tile keeps the compiler from hoisting every tile's
   // loads, which would push the score registers out to scratch.
   if (KSRC == KSRC_BF16) {
@@ -483,37 +489,43 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     }
     f32x4 bias = {0.f, 0.f, 0.f, 0.f};
     if (p.key_bias) bias = *reinterpret_cast<const f32x4*>(&sm.bias2[j0 + 4 * g]);
+    // Invisible keys are -inf, so they never pass a selection threshold (visible keys are finite: the
+    // staged bias is clamped). The scores are pinned here: otherwise the compiler sinks this
+    // epilogue to the next use and keeps both the MFMA accumulators and the bias values live for
+    // every tile.
+    if (j0 + 16 <= kmin) {  // the whole tile is visible to every row (wave-uniform)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = j0 + 4 * g + i;
-      const bool valid = j < nvis;
-      // visible keys are clamped to a finite floor (a -inf bias or a NaN becomes a zero probability);
-      // invisible keys are -inf, so they never pass a selection threshold
-      const float u = valid ? fmaxf(fmaf(acc[i], p.scale_log2, bias[i]), kNegBig) : -INFINITY;
-      // pinned here: otherwise the compiler sinks this epilogue to the next use and keeps both the
-      // MFMA accumulators and the bias values live for every tile
-      sc[t][i] = opaque(u);
-      const float uv = valid ? u : 0.f;
-      umax = fmaxf(umax, u);
-      umin = valid ? fminf(umin, u) : umin;
-      usum += uv;
-      usq = fmaf(uv, uv, usq);
+      for (int i = 0; i < 4; ++i) {
+        const float u = fmaf(acc[i], p.scale_log2, bias[i]);
+        sc[t][i] = opaque(u);
+        umax = fmaxf(umax, u);
+        umin = fminf(umin, u);
+        usum += u;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + 4 * g + i;
+        const bool valid = j < nvis;
+        const float u = valid ? fmaf(acc[i], p.scale_log2, bias[i]) : -INFINITY;
+        sc[t][i] = opaque(u);
+        umax = fmaxf(umax, u);
+        umin = valid ? fminf(umin, u) : umin;
+        usum += valid ? u : 0.f;
+      }
     }
     umax = opaque(umax);
     umin = opaque(umin);
     usum = opaque(usum);
-    usq = opaque(usq);
     __builtin_amdgcn_sched_barrier(0);
   }
   umax = row_max4(umax);
   umin = row_min4(umin);
   usum = row_sum4(usum);
-  usq = row_sum4(usq);
   if (g == 0) {
     sm.red_a[w][r] = umax;
     sm.red_b[w][r] = umin;
     sm.red_c[w][r] = usum;
-    sm.red_d[w][r] = usq;
   }
   // first segment overlapping this wave's keys
   int cs = 0;
@@ -521,22 +533,23 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   const int cs_first = cs;
   if (lane == 0) sm.cs0[w] = cs_first;
   __syncthreads();
-  float m = -INFINITY, mn = INFINITY, s1 = 0.f, s2 = 0.f;
+  float m = -INFINITY, mn = INFINITY, s1 = 0.f;
 #pragma unroll
   for (int ww = 0; ww < NW; ++ww) {
     m = fmaxf(m, sm.red_a[ww][r]);
     mn = fminf(mn, sm.red_b[ww][r]);
     s1 += sm.red_c[ww][r];
-    s2 += sm.red_d[ww][r];
   }
-  // Selection threshold: only keys at or above T enter the level-1 histogram. T sits kSelSigma
-  // standard deviations above the row mean, which keeps a few times more keys than the deepest rank
-  // (10 %) needs for bell-shaped rows; a row whose histogram ends up too small is redone with T = min.
+  // Selection threshold: only keys at or above T enter the level-1 histogram. The largest of n
+  // bell-shaped scores lies about sqrt(2 ln n) standard deviations above the mean, so T = mean +
+  // kSelSigma (max - mean) / sqrt(2 ln n) sits near kSelSigma deviations above the mean and keeps a
+  // few times more keys than the deepest rank (10 %) needs; a row whose histogram ends up too small
+  // is redone with T = min.
   float T = m;
   if (me0.ok) {
     const float mu = s1 / (float)nvis;
-    const float sd = sqrtf(fmaxf(s2 / (float)nvis - mu * mu, 0.f));
-    T = fmaxf(fminf(m, fmaf(kSelSigma, sd, mu)), mn);
+    const float c = kSelSigma * rsqrtf(fmaxf(2.f * logf((float)nvis), 1.f));
+    T = fmaxf(fminf(m, fmaf(c, m - mu, mu)), mn);
   } else {
     m = 0.f;
     mn = 0.f;
@@ -554,11 +567,11 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   __syncthreads();
 
   // ---- B: exponentials, entropy sum, segment masses and the level-1 histogram ---------------------
-  // Histogram counters pack a key count (bits 44..63) with a fixed-point mass f = round(e' 2^-33)
-  // (bits 0..43), e' = 2^(u - max + 64): f <= 2^31 per key, so a row of <= 8192 keys cannot carry
-  // out of the mass field. One LDS atomic per selected key updates both.
+  // Histogram counters pack a key count (bits 44..63) with a fixed-point mass f = round(e') (bits
+  // 0..43): f <= 2^31 per key, so a row of <= 8192 keys cannot carry out of the mass field. One LDS
+  // atomic per selected key updates both.
   {
-  const float off = 64.f - m;
+  const float off = kOff - m;
   float esum = 0.f, acc_seg = 0.f;
   int nb = (cs < p.n_seg) ? p.seg_bounds[cs + 1] : 0x7fffffff;
   const int gB = opaque(g);
@@ -647,8 +660,8 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   auto rc_z = [&]() { return sm.r_z[r]; };
   auto rc_T = [&]() { return sm.r_T[r]; };
   auto rc_k8 = [&]() { return sm.r_k8[r]; };
-  // p <= 2^-150 (an fp32 zero) <=> u - max + 64 - log2 Z' <= -150
-  auto rc_thr = [&]() { return sm.r_m[r] + log2f(sm.r_z[r]) - 214.f; };
+  // p <= 2^-150 (an fp32 zero) <=> u - max + kOff - log2 Z' <= -150
+  auto rc_thr = [&]() { return sm.r_m[r] + log2f(sm.r_z[r]) - (kOff + 150.f); };
 
   // region / frame / scalar outputs and target setup (wave w handles rows w and w + 8)
   for (int row = w; row < ROWS; row += NW) {
@@ -690,7 +703,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     }
     __syncthreads();
     if (sm.rfb[r]) {
-      const float mq = rc_m(), Tq = rc_T(), k8q = rc_k8(), offq = 64.f - mq;
+      const float mq = rc_m(), Tq = rc_T(), k8q = rc_k8(), offq = kOff - mq;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
 #pragma unroll
@@ -741,13 +754,15 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   const bool slow_path = sm.flag != 0;
   if (!slow_path) {
     {
-      // boundary bins of this lane's row (level-1 bins; bin1 returns 256 below the threshold)
+      // boundary bins of this lane's row (level-1 bins; keys below the threshold get bin 256). The
+      // list holds every key of a bin <= bq0 (the top-32 boundary bin and the bins above it: at most
+      // 31 + CAP keys) and of the other boundary bins.
       int bq[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) bq[t] = sm.ts[r][t].valid ? (int)sm.ts[r][t].prefix : -1;
-      // Two passes without returning atomics in the loop: count this lane's winners and candidates,
-      // reserve slots with one atomic each, then write.
-      int nw = 0, nc = 0;
+      // Two passes without returning atomics in the loop: count this lane's list keys, reserve slots
+      // with one atomic, then write.
+      int nc = 0;
       {
         const float mq = rc_m(), Tq = rc_T(), k8q = rc_k8();
 #pragma unroll
@@ -756,17 +771,14 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           for (int i = 0; i < 4; ++i) {
             const float u = sc[tt][i];
             const int dig = u >= Tq ? bin1(u, mq, k8q) : 256;
-            nw += dig < bq[0] ? 1 : 0;
-            nc += (dig == bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3]) ? 1 : 0;
+            nc += (dig <= bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3]) ? 1 : 0;
           }
-          nw = opaque(nw);
           nc = opaque(nc);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      int wpos = nw ? atomicAdd(&sm.nwin[r], nw) : 0;
       int cpos = nc ? atomicAdd(&sm.ncand[r], nc) : 0;
-      if (nw | nc) {
+      if (nc) {
         const int gq = opaque(g);
         const float mq = rc_m(), Tq = rc_T(), k8q = rc_k8();
 #pragma unroll
@@ -777,41 +789,36 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
             const int j = j0 + 4 * gq + i;
             const float u = sc[tt][i];
             const int dig = u >= Tq ? bin1(u, mq, k8q) : 256;
-            // a key can be both: ranked above the top-32 boundary and inside the boundary bin of a
-            // 1/5/10 % rank (at small n those ranks lie above rank 31)
-            if (dig < bq[0]) {
-              if (wpos < 32) {
-                sm.win_u[r][wpos] = u;
-                sm.win_j[r][wpos] = j;
-              }
-              ++wpos;
-            }
-            if (dig == bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3]) {
-              if (cpos < CAP) {
+            if (dig <= bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3]) {
+              if (cpos < CAPL) {
                 sm.u.sel.ce[r][cpos] = u;
                 sm.u.sel.cj[r][cpos] = j | (dig << 16);  // bin kept beside the index (j < 2^16)
               }
               ++cpos;
             }
           }
-          wpos = opaque(wpos);
           cpos = opaque(cpos);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
     __syncthreads();
-    // rank every candidate inside its bin
+    // rank every boundary-bin key inside its bin (the other keys of the bins above bq0 need none)
     for (int row = w; row < ROWS; row += NW) {
-      const int c = min(sm.ncand[row], CAP);
+      const int c = min(sm.ncand[row], CAPL);
+      const int b0 = sm.ts[row][0].valid ? (int)sm.ts[row][0].prefix : -1;
       for (int a = lane; a < c; a += 64) {
         const float ua = sm.u.sel.ce[row][a];
         const int ca = sm.u.sel.cj[row][a];
+        const int ba = ca >> 16;
         int rank = 0;
-        for (int q = 0; q < c; ++q) {
-          const float uq = sm.u.sel.ce[row][q];
-          const int cq = sm.u.sel.cj[row][q];
-          rank += ((cq >> 16) == (ca >> 16)) && ((uq > ua) || (uq == ua && cq < ca));
+        if (ba >= b0 || ba == (int)sm.ts[row][1].prefix || ba == (int)sm.ts[row][2].prefix ||
+            ba == (int)sm.ts[row][3].prefix) {
+          for (int q = 0; q < c; ++q) {
+            const float uq = sm.u.sel.ce[row][q];
+            const int cq = sm.u.sel.cj[row][q];
+            rank += ((cq >> 16) == (ca >> 16)) && ((uq > ua) || (uq == ua && cq < ca));
+          }
         }
         sm.u.sel.crank[row][a] = rank;
       }
@@ -820,14 +827,20 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     for (int row = w; row < ROWS; row += NW) {
       const float mr = sm.r_m[row];
       const RowInfo ri = row_info(p, b, hkv, rb, row);
-      const int c = min(sm.ncand[row], CAP);
+      const int c = min(sm.ncand[row], CAPL);
+      const int b0 = sm.ts[row][0].valid ? (int)sm.ts[row][0].prefix : -1;
       unsigned long long acc[NT] = {0ull, 0ull, 0ull, 0ull};
       for (int a = lane; a < c; a += 64) {
         const float ua = sm.u.sel.ce[row][a];
         const int ca = sm.u.sel.cj[row][a];
         const unsigned dga = (unsigned)(ca >> 16);
         const int rk = sm.u.sel.crank[row][a];
-        const float ea = __builtin_amdgcn_exp2f(fmaxf(ua + (64.f - mr), -256.f));
+        if ((int)dga < b0) {  // ranked above the top-32 boundary bin: one of the 32
+          const int slot = atomicAdd(&sm.nwin[row], 1);
+          sm.win_u[row][slot] = ua;
+          sm.win_j[row][slot] = ca & 0xFFFF;
+        }
+        const float ea = __builtin_amdgcn_exp2f(fmaxf(ua + (kOff - mr), -256.f));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const TState& ts = sm.ts[row][t];
@@ -848,8 +861,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       for (int t = 1; t < NT; ++t) {
         unsigned long long x = acc[t];
         for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-        if (lane == 0 && ri.ok)
-          sm.tmass[row][t - 1] = (float)(sm.ts[row][t].mass_before + x) * (0x1p33f / sm.r_z[row]);
+        if (lane == 0 && ri.ok) sm.tmass[row][t - 1] = (float)(sm.ts[row][t].mass_before + x) / sm.r_z[row];
       }
     }
     __syncthreads();
@@ -872,7 +884,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         const int ph = opaque(sm.ts[r][t].ph), sh = opaque(sm.ts[r][t].sh);
         const unsigned pre = opaque(sm.ts[r][t].prefix), dfix = opaque(sm.ts[r][t].dfix);
         const int gq = opaque(g);
-        const float mq = rc_m(), Tq = rc_T(), k32 = rc_k8() * 0x1p24f, offq = 64.f - mq;
+        const float mq = rc_m(), Tq = rc_T(), k32 = rc_k8() * 0x1p24f, offq = kOff - mq;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const int j0 = kbase + tt * 16;
@@ -1003,7 +1015,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
             const int jq = sm.u.sel.cj[row][q];
             rank += (Dq < Da) || (Dq == Da && jq < ja);
           }
-          sm.u.sel.sorted_e[row][rank] = __builtin_amdgcn_exp2f(fmaxf(ua + (64.f - mr), -256.f));
+          sm.u.sel.sorted_e[row][rank] = __builtin_amdgcn_exp2f(fmaxf(ua + (kOff - mr), -256.f));
           if (t == 0) {
             const int nsel = ts.target + 1;  // min(32, n)
             const int slot = ts.cnt_before + rank;
@@ -1028,7 +1040,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         a = wave_sum(a);
         if (lane == 0) {
           const float iz = 1.f / sm.r_z[row];
-          float mass = (float)ts.mass_before * (0x1p33f * iz) + a * iz;
+          float mass = (float)ts.mass_before * iz + a * iz;
           if (rr < c) mass += ts.frac * sm.u.sel.sorted_e[row][rr] * iz;
           sm.tmass[row][t - 1] = mass;
         }
@@ -1076,7 +1088,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     const RowInfo me2 = row_info(p, b, hkv, rb, r);
     if (w == 0 && g == 0 && me2.ok) {
       if (p.row_max) p.row_max[me2.grow] = rc_m() * kLn2;
-      if (p.row_lse) p.row_lse[me2.grow] = (rc_m() + log2f(rc_z()) - 64.f) * kLn2;
+      if (p.row_lse) p.row_lse[me2.grow] = (rc_m() + log2f(rc_z()) - kOff) * kLn2;
     }
   }
 
@@ -1119,7 +1131,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     const float pmul = kPScale / rc_z();
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
-      const float pm = opaque(pmul), offq = opaque(64.f - rc_m());  // recomputed per half, not hoisted per tile
+      const float pm = opaque(pmul), offq = opaque(kOff - rc_m());  // recomputed per half, not hoisted per tile
       const int rq = opaque(r), gq = opaque(g);  // likewise the per-key V offsets
       f32x4 oacc[4];
 #pragma unroll
@@ -1275,7 +1287,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         ref_tile(j0 + 16 * h2, u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pm = __builtin_amdgcn_exp2f(fmaxf(sc[t + h2][i] + (64.f - rc_m()), -256.f)) / rc_z();
+          const float pm = __builtin_amdgcn_exp2f(fmaxf(sc[t + h2][i] + (kOff - rc_m()), -256.f)) / rc_z();
           pv[h2][i] = pm;
           tv += fabsf(pm - __builtin_amdgcn_exp2f(u[i] - mref) * invZr);
         }
