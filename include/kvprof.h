@@ -163,7 +163,11 @@ typedef struct kvprof_args {
   size_t workspace_bytes;       /*   256-byte aligned (may be NULL when that size is 0)                */
 } kvprof_args;
 
-/* Workspace bytes kvprof_row_stats / kvprof_attend need for these arguments (0 for invalid ones). */
+/* Workspace bytes kvprof_row_stats / kvprof_attend need for these arguments (0 for invalid ones).
+ * Every call with at least one row needs some: a list of the 16-row blocks whose exact ranks take
+ * the slow path (4 bytes per block + 4), plus the decoded MXFP8 operands and, for heatmaps or
+ * histograms requested without their per-row inputs, those per-row arrays. The contents need no
+ * initialisation; concurrent calls must not share a workspace. */
 size_t kvprof_workspace_bytes(const kvprof_args* a);
 
 /* Row statistics over bf16 or MXFP8 scores (modes BF16 and MXFP8), optionally with O = P.V.

@@ -48,7 +48,7 @@ int check_mx_shape(const void* x, const void* codes, const void* scales, int64_t
 }
 
 struct Workspace {
-  size_t q_mx = 0, k_mx = 0, frame = 0, support = 0, region = 0, total = 0;
+  size_t q_mx = 0, k_mx = 0, frame = 0, support = 0, region = 0, redo = 0, total = 0;
 };
 
 int64_t total_rows(const kvprof_args* a) { return (int64_t)a->n_batch * a->n_heads_q * a->n_q; }
@@ -76,6 +76,11 @@ Workspace workspace_layout(const kvprof_args* a) {
       w.region = off;
       off += round256((size_t)rows * a->n_regions * 4);
     }
+  }
+  if (rows > 0 && a->n_heads_kv > 0) {  // redo list of the row kernel
+    w.redo = off;
+    const long long nb = kvp::row_blocks(a->n_batch, a->n_heads_kv, (a->n_heads_q / a->n_heads_kv) * a->n_q);
+    off += round256(kvp::redo_words(nb) * 4);
   }
   w.total = off;
   return w;
@@ -242,6 +247,7 @@ int run_rows(const kvprof_args* a, void* stream, bool need_o) {
   p.p_zero_frac = a->p_zero_frac;
   p.tv_p = a->tv_p;
   p.p_rowsum = a->p_rowsum;
+  p.redo = reinterpret_cast<unsigned*>(wsb + ws.redo);
   if (a->heatmap && !a->frame_mass) p.frame_mass = reinterpret_cast<float*>(wsb + ws.frame);
   if (a->hist) {
     if (!a->support) p.support = reinterpret_cast<float*>(wsb + ws.support);

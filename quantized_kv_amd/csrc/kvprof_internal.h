@@ -65,11 +65,19 @@ struct RowStatsParams {
   float* p_zero_frac;
   float* tv_p;
   float* p_rowsum;
+  // workspace: [0] = number of row blocks left to the redo kernel, [1 ..] = their logical ids
+  unsigned* redo;
 };
+
+// Words of the redo list for a problem of n_blocks row blocks.
+inline size_t redo_words(long long n_blocks) { return (size_t)n_blocks + 1; }
+inline long long row_blocks(int n_batch, int n_heads_kv, int rows_per_kv) {
+  return (long long)n_batch * n_heads_kv * ((rows_per_kv + 15) / 16);
+}
 
 enum KSrc { KSRC_BF16 = 0, KSRC_INT4 = 1 };
 
-// Main row kernel. tpw = 16-key tiles per wave (16 waves per workgroup, 16 rows per workgroup).
+// Main row kernel. tpw = 16-key tiles per wave (8 waves per workgroup, 16 rows per workgroup).
 hipError_t launch_row_stats(const RowStatsParams& p, int tpw, int ksrc, bool mx, hipStream_t s);
 int row_stats_tpw_for(int n_k, bool mx);  // tiles per wave this build uses for n_k keys, or -1
 

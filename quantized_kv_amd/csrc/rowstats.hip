@@ -32,13 +32,14 @@ constexpr int WGT = NW * 64;
 constexpr int ROWS = 16;
 constexpr int HB = 257;  // padded histogram stride (rows land in different LDS banks)
 constexpr int CAP = 256; // candidate slots per row (boundary bins)
-constexpr int CAPL = CAP + 32;  // fast-path list: the boundary bins plus the keys ranked above them
+constexpr int CAPL = CAP + 32;
+constexpr int kRedoGrid = 256;  // workgroups of the redo kernel (they loop over the redo list)  // fast-path list: the boundary bins plus the keys ranked above them
 constexpr float kOff = 31.f;    // e' = 2^(u - max + kOff): the largest key weighs 2^31
 constexpr int NT = 4;    // selected ranks per row
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kPScale = 32768.f;  // P is fed to the f16 MFMA as p * 2^15
-constexpr int kRing = 3;
+constexpr int kRing = 2;  // K tiles per wave in the LDS load ring (the load rate does not improve with more)
 constexpr unsigned long long kOne = 1ull << 44;            // one key in a packed histogram counter
 constexpr unsigned long long kMassMask = (1ull << 44) - 1;
 constexpr float kNegBig = -1.0e37f;  // floor of the staged key bias
@@ -87,6 +88,9 @@ struct Sel {
   };
 };
 
+// NL: score tiles of each wave kept in LDS instead of registers (the rest of the kernel needs the
+// registers they free).
+template <int NL>
 struct Smem {
   float red_a[NW][ROWS];
   float red_b[NW][ROWS];
@@ -106,11 +110,14 @@ struct Smem {
   int win_j[ROWS][32];
   int top0[ROWS];
   u32x4 qs[ROWS][17];  // Q rows as 16-byte chunks (B operand of S^T = K Q^T); padded against bank conflicts
-  float bias2[KVPROF_MAX_KEYS];  // key bias * log2(e)
+  f32x4 stash[NL > 0 ? NL : 1][NW][64];  // score tiles 0 .. NL-1 of every wave, one f32x4 per lane
   union {
     Sel sel;
     float ored[NW / 2][ROWS][64];
-    u32x4 ring[NW][kRing][4][64];  // per wave: kRing K tiles x 4 k-steps x 64 lanes (A fragments)
+    struct {
+      u32x4 ring[NW][kRing][4][64];  // per wave: kRing K tiles x 4 k-steps x 64 lanes (A fragments)
+      float rbias[NW][kRing][16];    // the tiles' raw key bias
+    } a;
   } u;
 };
 
@@ -319,7 +326,8 @@ __device__ __forceinline__ void init_target(TState& ts, int t, int n) {
 // Per-row scan of the level-1 histogram by one wave (lane holds bins 4*lane..4*lane+3): locates, for
 // every target of the row, the bin that holds its rank. A row whose histogram holds no more keys than
 // its deepest target is marked for a redo over every visible key.
-__device__ void scan_row(Smem& sm, int row, int lane) {
+template <typename SM>
+__device__ void scan_row(SM& sm, int row, int lane) {
   unsigned c[4];
   unsigned long long m[4];
 #pragma unroll
@@ -372,9 +380,21 @@ __device__ void scan_row(Smem& sm, int row, int lane) {
   }
 }
 
-template <int TPW, int KSRC, bool MX>
+template <int TPW>
+constexpr int stash_tiles() { return TPW == 49 ? 5 : 0; }
+
+// One workgroup = one row block (16 rows of one (batch, KV head)). SLOW = false: the main kernel, one
+// block per workgroup; a block whose exact ranks need the slow path is appended to the redo list
+// (p.redo) and finished by the SLOW = true kernel, which loops over that list and compiles the slow
+// path (its code would otherwise raise the register peak of the common case).
+template <int TPW, int KSRC, bool MX, bool SLOW>
 __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
-  __shared__ Smem sm;
+  constexpr int NL = stash_tiles<TPW>();
+  __shared__ Smem<NL> sm;
+  const int nblk = SLOW ? (int)p.redo[0] : 1;
+  for (int it = SLOW ? (int)blockIdx.x : 0; it < nblk; it += SLOW ? (int)gridDim.x : 1) {
+  const int bid = SLOW ? (int)p.redo[1 + it]
+                       : remap_block((int)blockIdx.x, p.n_batch * p.n_heads_kv * ((p.rows_per_kv + ROWS - 1) / ROWS));
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
@@ -382,8 +402,6 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   const int g = lane >> 4;  // key quad inside a 16-key tile
 
   const int nrb = (p.rows_per_kv + ROWS - 1) / ROWS;
-  const int nwg = p.n_batch * p.n_heads_kv * nrb;  // < 2^31 (checked on the host)
-  const int bid = remap_block((int)blockIdx.x, nwg);
   const int rb = bid % nrb;
   const int hkv = (bid / nrb) % p.n_heads_kv;
   const int b = bid / (nrb * p.n_heads_kv);
@@ -427,77 +445,81 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       sm.qs[r][c] = v;
     }
   }
-  // staged over the padded key range, so each lane reads its 4 bias values as one aligned 16-byte load
-  // (clamped to a finite floor: a -inf bias gives a zero probability, not an infinite score)
-  for (int j = tid; j < KVPROF_MAX_KEYS; j += WGT)
-    sm.bias2[j] = (p.key_bias && j < p.n_k) ? fmaxf(p.key_bias[j] * kLog2e, kNegBig) : 0.f;
   __syncthreads();
 
   // ---- A: scores ---------------------------------------------------------------------------------
   const int kbase = __builtin_amdgcn_readfirstlane(w * TPW * 16);  // wave-uniform: keep it scalar
-  float sc[TPW][4];
+  float sc[TPW - NL][4];  // tiles NL .. TPW-1 (tiles below NL live in sm.stash)
+  // score u of key 4g + i of tile t of this lane
+  auto scr = [&](int t, int i) -> float { return t < NL ? sm.stash[t][w][lane][i] : sc[t < NL ? 0 : t - NL][i]; };
   float umax = -INFINITY, umin = INFINITY, usum = 0.f;
+  // key bias: a buffer resource of 0 bytes when there is none (its loads return zero)
+  const rsrc_t rbs = make_rsrc(p.key_bias ? (const void*)p.key_bias : (const void*)p.q,
+                               p.key_bias ? (size_t)p.n_k * 4 : 0);
+  // Direct global->LDS loads (no VGPRs): tile t of this wave goes to ring slot t % kRing, each lane's
+  // 16 bytes landing at lane * 16, which is exactly its A-fragment; lanes 0..15 also load the tile's
+  // 16 bias values. The compiler does not track these writes, so the wait before reading a slot is
+  // explicit: loads retire in issue order, and the 5 (kRing - 1) loads of the later tiles may still
+  // be outstanding.
+  auto issue = [&](int t) {
+    const int slot = t % kRing;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)&sm.u.a.ring[w][slot][ks][0], 16,
+                                               (unsigned)((kbase + t * 16 + r) * KVPROF_HEAD_DIM + ks * 32 + 8 * g) * 2u, 0, 0, 0);
+    if (lane < 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (__attribute__((address_space(3))) void*)&sm.u.a.rbias[w][slot][0], 4,
+                                               (unsigned)(kbase + t * 16 + lane) * 4u, 0, 0, 0);
+  };
+  if (KSRC == KSRC_BF16) {
+#pragma unroll
+    for (int t = 0; t < kRing - 1 && t < TPW; ++t) issue(t);
+  }
   // The scheduling barrier at the end of each tile keeps the compiler from hoisting every tile's
   // loads, which would push the score registers out to scratch.
-  if (KSRC == KSRC_BF16) {
-    // Direct global->LDS loads (no VGPRs): tile t of this wave goes to ring slot t % kRing, each lane's
-    // 16 bytes landing at lane * 16, which is exactly its A-fragment. The compiler does not track
-    // these writes, so the wait before reading a slot is explicit: loads retire in issue order, and at
-    // most 4 * (kRing - 1) loads (the later tiles) may still be outstanding.
-#pragma unroll
-    for (int t = 0; t < kRing - 1 && t < TPW; ++t)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)&sm.u.ring[w][t % kRing][ks][0],
-                                                 16, (unsigned)((kbase + t * 16 + r) * KVPROF_HEAD_DIM + ks * 32 + 8 * g) * 2u, 0, 0, 0);
-  }
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int j0 = kbase + t * 16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 bias = {0.f, 0.f, 0.f, 0.f};
     if (KSRC == KSRC_BF16) {
-      if (t + kRing - 1 < TPW) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rk, (__attribute__((address_space(3))) void*)&sm.u.ring[w][(t + kRing - 1) % kRing][ks][0], 16,
-              (unsigned)((j0 + (kRing - 1) * 16 + r) * KVPROF_HEAD_DIM + ks * 32 + 8 * g) * 2u, 0, 0, 0);
-      }
-      constexpr int later = 4 * (kRing - 1);
-      const int pend = (TPW - 1 - t) < (kRing - 1) ? 4 * (TPW - 1 - t) : later;
-      // s_waitcnt vmcnt(pend), expcnt / lgkmcnt left alone (gfx9 encoding)
-      switch (pend) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-      }
+      if (t + kRing - 1 < TPW) issue(t + kRing - 1);
+      // s_waitcnt vmcnt(5 * later tiles in flight), expcnt / lgkmcnt left alone (gfx9 encoding)
+      if (t + kRing - 1 < TPW)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (5 * (kRing - 1)));
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);
       if (j0 < kmax) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          acc = mfma_step<KSRC>(sm.u.ring[w][t % kRing][ks][lane], sm.qs[r][ks * 4 + g], acc);
+          acc = mfma_step<KSRC>(sm.u.a.ring[w][t % kRing][ks][lane], sm.qs[r][ks * 4 + g], acc);
       }
-    } else if (j0 < kmax) {
-      u32x4 kf[4], kl[4];
+      bias = *reinterpret_cast<const f32x4*>(&sm.u.a.rbias[w][t % kRing][4 * g]);
+    } else {
+      if (j0 < kmax) {
+        u32x4 kf[4], kl[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[ks] = load_k<KSRC>(p, rk, L, j0 + r, ks * 32 + 8 * g, &kl[ks]);
+        for (int ks = 0; ks < 4; ++ks) kf[ks] = load_k<KSRC>(p, rk, L, j0 + r, ks * 32 + 8 * g, &kl[ks]);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        acc = mfma_step<KSRC>(kf[ks], sm.qs[r][ks * 4 + g], acc);
-        acc = mfma_step<KSRC>(kl[ks], sm.qs[r][ks * 4 + g], acc);
+        for (int ks = 0; ks < 4; ++ks) {
+          acc = mfma_step<KSRC>(kf[ks], sm.qs[r][ks * 4 + g], acc);
+          acc = mfma_step<KSRC>(kl[ks], sm.qs[r][ks * 4 + g], acc);
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)  // one dword each: a key past the end reads zero on its own
+        bias[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, (unsigned)(j0 + 4 * g + i) * 4u, 0, 0));
     }
-    f32x4 bias = {0.f, 0.f, 0.f, 0.f};
-    if (p.key_bias) bias = *reinterpret_cast<const f32x4*>(&sm.bias2[j0 + 4 * g]);
-    // Invisible keys are -inf, so they never pass a selection threshold (visible keys are finite: the
-    // staged bias is clamped). The scores are pinned here: otherwise the compiler sinks this
-    // epilogue to the next use and keeps both the MFMA accumulators and the bias values live for
-    // every tile.
+    // Invisible keys are -inf, so they never pass a selection threshold; visible keys are finite (a
+    // -inf bias is clamped: zero probability). The scores are pinned here: otherwise the compiler
+    // sinks this epilogue to the next use and keeps both the MFMA accumulators and the bias values
+    // live for every tile.
+    f32x4 ut;
     if (j0 + 16 <= kmin) {  // the whole tile is visible to every row (wave-uniform)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float u = fmaf(acc[i], p.scale_log2, bias[i]);
-        sc[t][i] = opaque(u);
+        const float u = fmaf(acc[i], p.scale_log2, fmaxf(bias[i] * kLog2e, kNegBig));
+        ut[i] = u;
         umax = fmaxf(umax, u);
         umin = fminf(umin, u);
         usum += u;
@@ -507,18 +529,25 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       for (int i = 0; i < 4; ++i) {
         const int j = j0 + 4 * g + i;
         const bool valid = j < nvis;
-        const float u = valid ? fmaf(acc[i], p.scale_log2, bias[i]) : -INFINITY;
-        sc[t][i] = opaque(u);
+        const float u = valid ? fmaf(acc[i], p.scale_log2, fmaxf(bias[i] * kLog2e, kNegBig)) : -INFINITY;
+        ut[i] = u;
         umax = fmaxf(umax, u);
         umin = valid ? fminf(umin, u) : umin;
         usum += valid ? u : 0.f;
       }
+    }
+    if (t < NL) {
+      sm.stash[t][w][lane] = ut;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[t < NL ? 0 : t - NL][i] = opaque(ut[i]);
     }
     umax = opaque(umax);
     umin = opaque(umin);
     usum = opaque(usum);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (KSRC == KSRC_BF16) __builtin_amdgcn_s_waitcnt(0x0F70);  // every ring load has landed
   umax = row_max4(umax);
   umin = row_min4(umin);
   usum = row_sum4(usum);
@@ -587,7 +616,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     float e[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float u = sc[t][i];
+      const float u = scr(t, i);
       const float tp = fmaxf(u + off, -256.f);
       e[i] = __builtin_amdgcn_exp2f(tp);
       esum = fmaf(e[i], tp, esum);
@@ -708,7 +737,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       for (int t = 0; t < TPW; ++t) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float u = sc[t][i];
+          const float u = scr(t, i);
           if (u >= Tq) {
             const float e = __builtin_amdgcn_exp2f(fmaxf(u + offq, -256.f));
             atomicAdd(&sm.u.sel.hist[r][bin1(u, mq, k8q)], kOne + (unsigned long long)fixmass(e));
@@ -752,6 +781,10 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   }
   __syncthreads();
   const bool slow_path = sm.flag != 0;
+  if (!SLOW && slow_path && tid == 0) {  // left to the redo kernel, which rewrites every output
+    const unsigned k = atomicAdd(p.redo, 1u);
+    p.redo[1 + k] = (unsigned)bid;
+  }
   if (!slow_path) {
     {
       // boundary bins of this lane's row (level-1 bins; keys below the threshold get bin 256). The
@@ -769,7 +802,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         for (int tt = 0; tt < TPW; ++tt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float u = sc[tt][i];
+            const float u = scr(tt, i);
             const int dig = u >= Tq ? bin1(u, mq, k8q) : 256;
             nc += (dig <= bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3]) ? 1 : 0;
           }
@@ -787,7 +820,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int j = j0 + 4 * gq + i;
-            const float u = sc[tt][i];
+            const float u = scr(tt, i);
             const int dig = u >= Tq ? bin1(u, mq, k8q) : 256;
             if (dig <= bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3]) {
               if (cpos < CAPL) {
@@ -865,7 +898,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       }
     }
     __syncthreads();
-  } else {
+  } else if (SLOW) {
   // ---- D: refine and gather, one target at a time --------------------------------------------------
 #pragma unroll 1
   for (int t = 0; t < NT; ++t) {
@@ -891,7 +924,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int j = j0 + 4 * gq + i;
-            const float u = sc[tt][i];
+            const float u = scr(tt, i);
             if (u >= Tq) {
               const unsigned D = dkey32(u, mq, k32);
               if (ts_in(D, j, ph, sh, pre, dfix)) {
@@ -977,7 +1010,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = j0 + 4 * gq + i;
-          const float u = sc[tt][i];
+          const float u = scr(tt, i);
           if (u >= Tq) {
             const unsigned D = dkey32(u, mq, k32);
             if (ts_in(D, j, ph, sh, pre, dfix)) {
@@ -1109,7 +1142,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = j0 + 4 * gq + i;
-          cnt += (j < nv && sc[t][i] <= thr_u) ? 1 : 0;
+          cnt += (j < nv && scr(t, i) <= thr_u) ? 1 : 0;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1142,7 +1175,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         if (j0 < kmax) {
         f16x4 pa;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pa[i] = (_Float16)(__builtin_amdgcn_exp2f(fmaxf(sc[t][i] + offq, -256.f)) * pm);
+        for (int i = 0; i < 4; ++i) pa[i] = (_Float16)(__builtin_amdgcn_exp2f(fmaxf(scr(t, i) + offq, -256.f)) * pm);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int c = half * 64 + db * 16 + rq;
@@ -1206,7 +1239,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = j0 + 4 * g + i;
-        float bb = (j < p.n_k) ? sm.bias2[j] : 0.f;
+        float bb = (p.key_bias && j < p.n_k) ? fmaxf(p.key_bias[j] * kLog2e, kNegBig) : 0.f;
         u[i] = j < nvis ? fmaf(acc[i], p.scale_log2, bb) : -INFINITY;
       }
     };
@@ -1287,7 +1320,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         ref_tile(j0 + 16 * h2, u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pm = __builtin_amdgcn_exp2f(fmaxf(sc[t + h2][i] + (kOff - rc_m()), -256.f)) / rc_z();
+          const float pm = __builtin_amdgcn_exp2f(fmaxf(scr(t + h2, i) + (kOff - rc_m()), -256.f)) / rc_z();
           pv[h2][i] = pm;
           tv += fabsf(pm - __builtin_amdgcn_exp2f(u[i] - mref) * invZr);
         }
@@ -1342,6 +1375,12 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       if (p.argmax_ref) p.argmax_ref[me.grow] = aref;
     }
   }
+  if (SLOW) __syncthreads();  // the next block reuses the shared memory
+  }
+}
+
+__global__ void redo_reset(unsigned* redo) {
+  if (threadIdx.x == 0) redo[0] = 0u;
 }
 
 template <int TPW, int KSRC, bool MX>
@@ -1349,7 +1388,9 @@ hipError_t launch_t(const RowStatsParams& p, hipStream_t s) {
   const int nrb = (p.rows_per_kv + ROWS - 1) / ROWS;
   const long long nwg = (long long)p.n_batch * p.n_heads_kv * nrb;
   if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL((row_kernel<TPW, KSRC, MX>), dim3((unsigned)nwg), dim3(WGT), 0, s, p);
+  hipLaunchKernelGGL(redo_reset, dim3(1), dim3(64), 0, s, p.redo);
+  hipLaunchKernelGGL((row_kernel<TPW, KSRC, MX, false>), dim3((unsigned)nwg), dim3(WGT), 0, s, p);
+  hipLaunchKernelGGL((row_kernel<TPW, KSRC, MX, true>), dim3((unsigned)(nwg < kRedoGrid ? nwg : kRedoGrid)), dim3(WGT), 0, s, p);
   return hipGetLastError();
 }
 

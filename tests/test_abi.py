@@ -105,8 +105,13 @@ def test_region_and_workspace_validation(lib):
     rb = (ctypes.c_int32 * 3)(0, 200, 100)
     a = _args(n_regions=2, region_bounds=rb)
     assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_ESHAPE
-    # too many tiny segments inside one wave's key slice
+    # every call with rows needs a workspace (the redo list of the row kernel)
     a = _args(n_frames=64, frame_len=2, frame_mass=0x30000)
+    need = lib.kvprof_workspace_bytes(ctypes.byref(a))
+    assert need >= 4 * (1 + 1)
+    assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_ESIZE
+    # too many tiny segments inside one wave's key slice (validation never touches the workspace)
+    a.workspace, a.workspace_bytes = 0x40000, need
     assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_EUNSUPPORTED
     # MX mode needs a workspace for the decoded Q/K
     a = _args(mode=B.MODE_MXFP8, q_codes=1, q_scales=1, k_codes=1, k_scales=1)
