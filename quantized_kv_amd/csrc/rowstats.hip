@@ -32,8 +32,8 @@ constexpr int WGT = NW * 64;
 constexpr int ROWS = 16;
 constexpr int HB = 257;  // padded histogram stride (rows land in different LDS banks)
 constexpr int CAP = 256; // candidate slots per row (boundary bins)
-constexpr int CAPL = CAP + 32;
-constexpr int kRedoGrid = 256;  // workgroups of the redo kernel (they loop over the redo list)  // fast-path list: the boundary bins plus the keys ranked above them
+constexpr int CAPL = CAP + 32;   // fast-path list: the boundary bins plus the keys ranked above them
+constexpr int kRedoGrid = 256;  // workgroups of the redo kernel (they loop over the redo list)
 constexpr float kOff = 31.f;    // e' = 2^(u - max + kOff): the largest key weighs 2^31
 constexpr int NT = 4;    // selected ranks per row
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -659,24 +659,25 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   for (int row = w; row < ROWS; row += NW) {
     const RowInfo ri = row_info(p, b, hkv, rb, row);
     const int span = TPW * 16;
+    float zpart = 0.f;
     for (int s = lane; s < p.n_seg; s += 64) {
       float v = 0.f;
       const int s0 = p.seg_bounds[s], s1_ = p.seg_bounds[s + 1];
+#pragma unroll
       for (int ww = 0; ww < NW; ++ww) {
         const int w0 = ww * span, w1 = w0 + span;
-        if (w0 < s1_ && w1 > s0) {
-          const int slot = s - sm.cs0[ww];
-          if (slot >= 0 && slot < kSegPerWave) v += sm.segpart[ww][row][slot];
-        }
+        const int slot = s - sm.cs0[ww];
+        const bool hit = w0 < s1_ && w1 > s0 && slot >= 0 && slot < kSegPerWave;
+        const float x = sm.segpart[ww][row][hit ? slot : 0];
+        v += hit ? x : 0.f;
       }
       sm.segmass[row][s] = v;
+      zpart += v;
     }
-    __syncthreads();  // (uniform: every wave runs this block)
+    // fixed-order wave reductions: Z' over the segments, the entropy sum over the waves
+    float z = wave_sum(zpart);
+    const float e_ = wave_sum(lane < NW ? sm.red_e[lane < NW ? lane : 0][row] : 0.f);
     if (lane == 0) {
-      float z = 0.f;
-      for (int s = 0; s < p.n_seg; ++s) z += sm.segmass[row][s];
-      float e_ = 0.f;
-      for (int ww = 0; ww < NW; ++ww) e_ += sm.red_e[ww][row];
       if (!ri.ok || !(z > 0.f)) z = 1.f;
       sm.r_z[row] = z;
       sm.r_e[row] = e_;
@@ -698,18 +699,16 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     if (ri.ok) {
       const float z = sm.r_z[row];
       const float iz = 1.f / z;
-      if (lane < p.n_regions) {
-        float a = 0.f;
-        for (int s = 0; s < p.n_seg; ++s)
-          if (p.seg_region[s] == lane) a += sm.segmass[row][s];
-        if (p.region_mass) p.region_mass[ri.grow * p.n_regions + lane] = a * iz;
+      // lane q < n_regions sums region q, lane q < n_frames frame q (segments in key order)
+      float ar = 0.f, af = 0.f;
+#pragma unroll 8
+      for (int s = 0; s < p.n_seg; ++s) {
+        const float x = sm.segmass[row][s];
+        ar += p.seg_region[s] == lane ? x : 0.f;
+        af += p.seg_frame[s] == lane ? x : 0.f;
       }
-      for (int f = lane; f < p.n_frames; f += 64) {
-        float a = 0.f;
-        for (int s = 0; s < p.n_seg; ++s)
-          if (p.seg_frame[s] == f) a += sm.segmass[row][s];
-        if (p.frame_mass) p.frame_mass[ri.grow * p.n_frames + f] = a * iz;
-      }
+      if (p.region_mass && lane < p.n_regions) p.region_mass[ri.grow * p.n_regions + lane] = ar * iz;
+      if (p.frame_mass && lane < p.n_frames) p.frame_mass[ri.grow * p.n_frames + lane] = af * iz;
     }
     if (lane < NT) init_target(sm.ts[row][lane], lane, ri.ok ? ri.nvis : 0);
   }
@@ -836,24 +835,31 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       }
     }
     __syncthreads();
-    // rank every boundary-bin key inside its bin (the other keys of the bins above bq0 need none)
+    // rank every boundary-bin key inside its bin (the other keys of the bins above bq0 need none):
+    // lane a takes entry a; the list is read back four entries at a time (broadcast loads)
     for (int row = w; row < ROWS; row += NW) {
-      const int c = min(sm.ncand[row], CAPL);
+      const int c = __builtin_amdgcn_readfirstlane(min(sm.ncand[row], CAPL));
       const int b0 = sm.ts[row][0].valid ? (int)sm.ts[row][0].prefix : -1;
-      for (int a = lane; a < c; a += 64) {
-        const float ua = sm.u.sel.ce[row][a];
-        const int ca = sm.u.sel.cj[row][a];
+      const int b1 = (int)sm.ts[row][1].prefix, b2 = (int)sm.ts[row][2].prefix, b3 = (int)sm.ts[row][3].prefix;
+      for (int a0 = 0; a0 < c; a0 += 64) {
+        const int a = a0 + lane;
+        const float ua = a < c ? sm.u.sel.ce[row][a] : 0.f;
+        const int ca = a < c ? sm.u.sel.cj[row][a] : -1;
         const int ba = ca >> 16;
         int rank = 0;
-        if (ba >= b0 || ba == (int)sm.ts[row][1].prefix || ba == (int)sm.ts[row][2].prefix ||
-            ba == (int)sm.ts[row][3].prefix) {
-          for (int q = 0; q < c; ++q) {
-            const float uq = sm.u.sel.ce[row][q];
-            const int cq = sm.u.sel.cj[row][q];
-            rank += ((cq >> 16) == (ca >> 16)) && ((uq > ua) || (uq == ua && cq < ca));
+#pragma unroll 4
+        for (int q = 0; q < c; q += 4) {
+          const f32x4 u4 = *reinterpret_cast<const f32x4*>(&sm.u.sel.ce[row][q]);
+          const u32x4 c4 = *reinterpret_cast<const u32x4*>(&sm.u.sel.cj[row][q]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // bitwise, not short-circuit: no branches in the loop
+            const int cq = (int)c4[e];
+            rank += (int)(q + e < c) & (int)((cq >> 16) == ba) & ((int)(u4[e] > ua) | ((int)(u4[e] == ua) & (int)(cq < ca)));
           }
         }
-        sm.u.sel.crank[row][a] = rank;
+        const bool need = ba >= b0 || ba == b1 || ba == b2 || ba == b3;
+        if (a < c) sm.u.sel.crank[row][a] = need ? rank : 0;
       }
     }
     __syncthreads();
