@@ -456,17 +456,22 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   // key bias: a buffer resource of 0 bytes when there is none (its loads return zero)
   const rsrc_t rbs = make_rsrc(p.key_bias ? (const void*)p.key_bias : (const void*)p.q,
                                p.key_bias ? (size_t)p.n_k * 4 : 0);
-  // Direct global->LDS loads (no VGPRs): tile t of this wave goes to ring slot t % kRing, each lane's
-  // 16 bytes landing at lane * 16, which is exactly its A-fragment; lanes 0..15 also load the tile's
-  // 16 bias values. The compiler does not track these writes, so the wait before reading a slot is
-  // explicit: loads retire in issue order, and the 5 (kRing - 1) loads of the later tiles may still
-  // be outstanding.
+  // Direct global->LDS loads (no VGPRs) of tile t into ring slot t % kRing. Load ks brings keys
+  // 4ks .. 4ks+3 of the tile whole (lane l: key 4ks + l/16, 16-byte chunk l%16 of its LDS row), so
+  // every load reads complete cache lines; the chunk stored at position q of key k's row is chunk
+  // q ^ k, which makes the A-fragment reads below free of bank conflicts. Lanes 0..15 also load the
+  // tile's 16 bias values. The compiler does not track these writes, so the wait before reading a
+  // slot is explicit: loads retire in issue order, and the 5 (kRing - 1) loads of the later tiles
+  // may still be outstanding.
   auto issue = [&](int t) {
     const int slot = t % kRing;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kt = 4 * ks + (lane >> 4);  // key inside the tile
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)&sm.u.a.ring[w][slot][ks][0], 16,
-                                               (unsigned)((kbase + t * 16 + r) * KVPROF_HEAD_DIM + ks * 32 + 8 * g) * 2u, 0, 0, 0);
+                                               (unsigned)((kbase + t * 16 + kt) * (KVPROF_HEAD_DIM * 2) + (((lane & 15) ^ kt) * 16)),
+                                               0, 0, 0);
+    }
     if (lane < 16)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (__attribute__((address_space(3))) void*)&sm.u.a.rbias[w][slot][0], 4,
                                                (unsigned)(kbase + t * 16 + lane) * 4u, 0, 0, 0);
@@ -491,8 +496,8 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         __builtin_amdgcn_s_waitcnt(0x0F70);
       if (j0 < kmax) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          acc = mfma_step<KSRC>(sm.u.a.ring[w][t % kRing][ks][lane], sm.qs[r][ks * 4 + g], acc);
+        for (int ks = 0; ks < 4; ++ks)  // chunk 4ks + g of key r (see issue)
+          acc = mfma_step<KSRC>(sm.u.a.ring[w][t % kRing][r >> 2][(r & 3) * 16 + ((4 * ks + g) ^ r)], sm.qs[r][ks * 4 + g], acc);
       }
       bias = *reinterpret_cast<const f32x4*>(&sm.u.a.rbias[w][t % kRing][4 * g]);
     } else {
