@@ -85,6 +85,7 @@ struct Sel {
   union {
     float sorted_e[ROWS][CAP];  // slow path: candidate e' by rank
     int crank[ROWS][CAPL];      // fast path: rank of a candidate inside its level-1 bin
+    unsigned gbits[7][NW][64];  // fast-path gather: list membership of each lane's keys, 32 per word
   };
 };
 
@@ -797,39 +798,45 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       int bq[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) bq[t] = sm.ts[r][t].valid ? (int)sm.ts[r][t].prefix : -1;
-      // Two passes without returning atomics in the loop: count this lane's list keys, reserve slots
-      // with one atomic, then write.
+      // Two passes without returning atomics in the loop: mark and count this lane's list keys (one
+      // bit per key, 8 tiles per word, kept in LDS), reserve slots with one atomic, then write.
+      static_assert((TPW + 7) / 8 <= 7, "gather bit words");
       int nc = 0;
       {
         const float mq = rc_m(), Tq = rc_T(), k8q = rc_k8();
+        unsigned bits = 0u;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float u = scr(tt, i);
             const int dig = u >= Tq ? bin1(u, mq, k8q) : 256;
-            nc += (dig <= bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3]) ? 1 : 0;
+            const bool in = (dig <= bq[0]) | (dig == bq[1]) | (dig == bq[2]) | (dig == bq[3]);
+            bits |= in ? 1u << (4 * (tt & 7) + i) : 0u;
           }
-          nc = opaque(nc);
+          if ((tt & 7) == 7 || tt == TPW - 1) {
+            sm.u.sel.gbits[tt >> 3][w][lane] = bits;
+            nc += __builtin_popcount(bits);
+            bits = 0u;
+          }
+          bits = opaque(bits);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       int cpos = nc ? atomicAdd(&sm.ncand[r], nc) : 0;
       if (nc) {
         const int gq = opaque(g);
-        const float mq = rc_m(), Tq = rc_T(), k8q = rc_k8();
+        unsigned bits = 0u;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const int j0 = kbase + tt * 16;
+          if ((tt & 7) == 0) bits = sm.u.sel.gbits[tt >> 3][w][lane];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int j = j0 + 4 * gq + i;
-            const float u = scr(tt, i);
-            const int dig = u >= Tq ? bin1(u, mq, k8q) : 256;
-            if (dig <= bq[0] || dig == bq[1] || dig == bq[2] || dig == bq[3]) {
+            if ((bits >> (4 * (tt & 7) + i)) & 1u) {
               if (cpos < CAPL) {
-                sm.u.sel.ce[r][cpos] = u;
-                sm.u.sel.cj[r][cpos] = j | (dig << 16);  // bin kept beside the index (j < 2^16)
+                sm.u.sel.ce[r][cpos] = scr(tt, i);
+                sm.u.sel.cj[r][cpos] = j0 + 4 * gq + i;
               }
               ++cpos;
             }
@@ -844,6 +851,10 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     // lane a takes entry a; the list is read back four entries at a time (broadcast loads)
     for (int row = w; row < ROWS; row += NW) {
       const int c = __builtin_amdgcn_readfirstlane(min(sm.ncand[row], CAPL));
+      {  // tag each entry with its level-1 bin (this wave alone reads and writes the row's list)
+        const float mr = sm.r_m[row], k8r = sm.r_k8[row];
+        for (int a = lane; a < c; a += 64) sm.u.sel.cj[row][a] |= bin1(sm.u.sel.ce[row][a], mr, k8r) << 16;
+      }
       const int b0 = sm.ts[row][0].valid ? (int)sm.ts[row][0].prefix : -1;
       const int b1 = (int)sm.ts[row][1].prefix, b2 = (int)sm.ts[row][2].prefix, b3 = (int)sm.ts[row][3].prefix;
       for (int a0 = 0; a0 < c; a0 += 64) {
