@@ -187,16 +187,17 @@ __device__ __forceinline__ float bin_scale(float m, float T) {
   const float d = m - T;
   return (d > 1e-20f && d < 1e30f) ? 256.f / d : 0.f;  // 0: every key in bin 0 (ranked by index)
 }
-__device__ __forceinline__ int bin1(float u, float m, float k8) {
-  return (int)fminf(__fmul_rn(__fsub_rn(m, u), k8), 255.f);
+// x = (max - u) k8 as one rounding: fma(-u, k8, mk8) with mk8 = round(max k8). Monotone in u.
+__device__ __forceinline__ int bin1(float u, float k8, float mk8) {
+  return (int)fminf(__fmaf_rn(-u, k8, mk8), 255.f);  // (a tiny negative x truncates to bin 0)
 }
-// 32-bit order key for the refinement levels: the same quantity scaled by 2^24 (an exact power of
-// two, so key >> 24 is the level-1 bin).
-__device__ __forceinline__ unsigned dkey32(float u, float m, float k32) {
-  return (unsigned)fminf(__fmul_rn(__fsub_rn(m, u), k32), 4294967040.f);
+// 32-bit order key for the refinement levels: the same quantity scaled by 2^24 (k32 = k8 2^24,
+// mk32 = mk8 2^24, exact powers of two, so key >> 24 is the level-1 bin).
+__device__ __forceinline__ unsigned dkey32(float u, float k32, float mk32) {
+  return (unsigned)fminf(fmaxf(__fmaf_rn(-u, k32, mk32), 0.f), 4294967040.f);
 }
-// Fixed-point mass of a key: round(e') <= 2^31.
-__device__ __forceinline__ unsigned fixmass(float e) { return (unsigned)(e + 0.5f); }
+// Fixed-point mass of a key: trunc(e') <= 2^31 (an error below 2^-31 of the largest key's weight).
+__device__ __forceinline__ unsigned fixmass(float e) { return (unsigned)e; }
 constexpr int kSh = 24;  // level-1 bin = key >> 24
 
 __device__ __forceinline__ int remap_block(int bid, int n) {
@@ -610,7 +611,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   float esum = 0.f, acc_seg = 0.f;
   int nb = (cs < p.n_seg) ? p.seg_bounds[cs + 1] : 0x7fffffff;
   const int gB = opaque(g);
-  const float Tq = opaque(T), k8q = opaque(k8), mq = opaque(m);
+  const float Tq = opaque(T), k8q = opaque(k8), mk8q = opaque(__fmul_rn(m, k8));
   auto flush = [&](float a, int seg) {
     float v = row_sum4(a);
     if (g == 0 && seg - cs_first < kSegPerWave) sm.segpart[w][r][seg - cs_first] = v;
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       e[i] = __builtin_amdgcn_exp2f(tp);
       esum = fmaf(e[i], tp, esum);
       if (u >= Tq)
-        atomicAdd(&sm.u.sel.hist[r][bin1(u, mq, k8q)], kOne + (unsigned long long)fixmass(e[i]));
+        atomicAdd(&sm.u.sel.hist[r][bin1(u, k8q, mk8q)], kOne + (unsigned long long)fixmass(e[i]));
     }
     if (j0 + 16 <= nb) {
       acc_seg += (e[0] + e[1]) + (e[2] + e[3]);
@@ -737,7 +738,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     }
     __syncthreads();
     if (sm.rfb[r]) {
-      const float mq = rc_m(), Tq = rc_T(), k8q = rc_k8(), offq = kOff - mq;
+      const float mq = rc_m(), Tq = rc_T(), k8q = rc_k8(), offq = kOff - mq, mk8q = __fmul_rn(mq, k8q);
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
 #pragma unroll
@@ -745,7 +746,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           const float u = scr(t, i);
           if (u >= Tq) {
             const float e = __builtin_amdgcn_exp2f(fmaxf(u + offq, -256.f));
-            atomicAdd(&sm.u.sel.hist[r][bin1(u, mq, k8q)], kOne + (unsigned long long)fixmass(e));
+            atomicAdd(&sm.u.sel.hist[r][bin1(u, k8q, mk8q)], kOne + (unsigned long long)fixmass(e));
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -803,14 +804,14 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       static_assert((TPW + 7) / 8 <= 7, "gather bit words");
       int nc = 0;
       {
-        const float mq = rc_m(), Tq = rc_T(), k8q = rc_k8();
+        const float Tq = rc_T(), k8q = rc_k8(), mk8q = __fmul_rn(rc_m(), k8q);
         unsigned bits = 0u;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float u = scr(tt, i);
-            const int dig = u >= Tq ? bin1(u, mq, k8q) : 256;
+            const int dig = u >= Tq ? bin1(u, k8q, mk8q) : 256;
             const bool in = (dig <= bq[0]) | (dig == bq[1]) | (dig == bq[2]) | (dig == bq[3]);
             bits |= in ? 1u << (4 * (tt & 7) + i) : 0u;
           }
@@ -833,11 +834,9 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           if ((tt & 7) == 0) bits = sm.u.sel.gbits[tt >> 3][w][lane];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            if ((bits >> (4 * (tt & 7) + i)) & 1u) {
-              if (cpos < CAPL) {
-                sm.u.sel.ce[r][cpos] = scr(tt, i);
-                sm.u.sel.cj[r][cpos] = j0 + 4 * gq + i;
-              }
+            if ((bits >> (4 * (tt & 7) + i)) & 1u) {  // (the fast path holds <= 31 + CAP < CAPL keys)
+              sm.u.sel.ce[r][cpos] = scr(tt, i);
+              sm.u.sel.cj[r][cpos] = j0 + 4 * gq + i;
               ++cpos;
             }
           }
@@ -852,8 +851,8 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     for (int row = w; row < ROWS; row += NW) {
       const int c = __builtin_amdgcn_readfirstlane(min(sm.ncand[row], CAPL));
       {  // tag each entry with its level-1 bin (this wave alone reads and writes the row's list)
-        const float mr = sm.r_m[row], k8r = sm.r_k8[row];
-        for (int a = lane; a < c; a += 64) sm.u.sel.cj[row][a] |= bin1(sm.u.sel.ce[row][a], mr, k8r) << 16;
+        const float k8r = sm.r_k8[row], mk8r = __fmul_rn(sm.r_m[row], k8r);
+        for (int a = lane; a < c; a += 64) sm.u.sel.cj[row][a] |= bin1(sm.u.sel.ce[row][a], k8r, mk8r) << 16;
       }
       const int b0 = sm.ts[row][0].valid ? (int)sm.ts[row][0].prefix : -1;
       const int b1 = (int)sm.ts[row][1].prefix, b2 = (int)sm.ts[row][2].prefix, b3 = (int)sm.ts[row][3].prefix;
@@ -940,6 +939,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         const unsigned pre = opaque(sm.ts[r][t].prefix), dfix = opaque(sm.ts[r][t].dfix);
         const int gq = opaque(g);
         const float mq = rc_m(), Tq = rc_T(), k32 = rc_k8() * 0x1p24f, offq = kOff - mq;
+        const float mk32 = __fmul_rn(mq, rc_k8()) * 0x1p24f;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const int j0 = kbase + tt * 16;
@@ -948,7 +948,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
             const int j = j0 + 4 * gq + i;
             const float u = scr(tt, i);
             if (u >= Tq) {
-              const unsigned D = dkey32(u, mq, k32);
+              const unsigned D = dkey32(u, k32, mk32);
               if (ts_in(D, j, ph, sh, pre, dfix)) {
                 const int dig = (int)(((ph ? (unsigned)j : D) >> (sh - 8)) & 255u);
                 const float e = __builtin_amdgcn_exp2f(fmaxf(u + offq, -256.f));
@@ -1025,7 +1025,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       const int ph = opaque(sm.ts[r][t].ph), sh = opaque(sm.ts[r][t].sh);
       const unsigned pre = opaque(sm.ts[r][t].prefix), dfix = opaque(sm.ts[r][t].dfix);
       const int gq = opaque(g);
-      const float mq = rc_m(), Tq = rc_T(), k32 = rc_k8() * 0x1p24f;
+      const float Tq = rc_T(), k32 = rc_k8() * 0x1p24f, mk32 = __fmul_rn(rc_m(), rc_k8()) * 0x1p24f;
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt) {
         const int j0 = kbase + tt * 16;
@@ -1034,7 +1034,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           const int j = j0 + 4 * gq + i;
           const float u = scr(tt, i);
           if (u >= Tq) {
-            const unsigned D = dkey32(u, mq, k32);
+            const unsigned D = dkey32(u, k32, mk32);
             if (ts_in(D, j, ph, sh, pre, dfix)) {
               const int slot = atomicAdd(&sm.ncand[r], 1);
               if (slot < CAP) {
@@ -1058,15 +1058,15 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     for (int row = w; row < ROWS; row += NW) {
       const TState ts = sm.ts[row][t];
       const int c = min(sm.ncand[row], CAP);
-      const float mr = sm.r_m[row], k32r = sm.r_k8[row] * 0x1p24f;
+      const float mr = sm.r_m[row], k32r = sm.r_k8[row] * 0x1p24f, mk32r = __fmul_rn(mr, sm.r_k8[row]) * 0x1p24f;
       if (ts.valid) {
         for (int a = lane; a < c; a += 64) {
           const float ua = sm.u.sel.ce[row][a];
           const int ja = sm.u.sel.cj[row][a];
-          const unsigned Da = dkey32(ua, mr, k32r);
+          const unsigned Da = dkey32(ua, k32r, mk32r);
           int rank = 0;
           for (int q = 0; q < c; ++q) {
-            const unsigned Dq = dkey32(sm.u.sel.ce[row][q], mr, k32r);
+            const unsigned Dq = dkey32(sm.u.sel.ce[row][q], k32r, mk32r);
             const int jq = sm.u.sel.cj[row][q];
             rank += (Dq < Da) || (Dq == Da && jq < ja);
           }
