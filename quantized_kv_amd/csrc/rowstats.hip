@@ -107,8 +107,8 @@ struct Smem {
   TState ts[ROWS][NT];
   float tmass[ROWS][3];
   int ncand[ROWS], nwin[ROWS];
-  float win_u[ROWS][32];  // scores of the top-32 keys
-  int win_j[ROWS][32];
+  alignas(16) float win_u[ROWS][32];  // scores of the top-32 keys
+  alignas(16) int win_j[ROWS][32];
   int top0[ROWS];
   u32x4 qs[ROWS][17];  // Q rows as 16-byte chunks (B operand of S^T = K Q^T); padded against bank conflicts
   f32x4 stash[NL > 0 ? NL : 1][NW][64];  // score tiles 0 .. NL-1 of every wave, one f32x4 per lane
@@ -768,18 +768,27 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   if (tid == 0) sm.flag = 0;
   __syncthreads();
   for (int row = w; row < ROWS; row += NW) {
-    if (lane == 0) {
-      int tot = 0, bad = 0;
-      for (int t = 0; t < NT; ++t) {
-        const TState& ts = sm.ts[row][t];
-        if (!ts.valid) continue;  // row past the end
-        if (!ts.resolved) bad = 1;
-        bool seen = false;
-        for (int q = 0; q < t; ++q) seen |= sm.ts[row][q].valid && sm.ts[row][q].prefix == ts.prefix;
-        if (!seen) tot += ts.cnt_in;
-      }
-      if (bad || tot > CAP) atomicOr(&sm.flag, 1);
+    // all four states read at once (one LDS round trip), then a wave-uniform test
+    unsigned pv[NT];
+    int cin[NT], val[NT], res[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      pv[t] = sm.ts[row][t].prefix;
+      cin[t] = sm.ts[row][t].cnt_in;
+      val[t] = sm.ts[row][t].valid;
+      res[t] = sm.ts[row][t].resolved;
     }
+    int tot = 0, bad = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (!val[t]) continue;  // row past the end
+      bad |= !res[t];
+      bool seen = false;
+#pragma unroll
+      for (int q = 0; q < t; ++q) seen |= val[q] && pv[q] == pv[t];
+      tot += seen ? 0 : cin[t];
+    }
+    if (lane == 0 && (bad || tot > CAP)) atomicOr(&sm.flag, 1);
   }
   if (tid < ROWS) {
     sm.ncand[tid] = 0;
@@ -827,6 +836,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       int cpos = nc ? atomicAdd(&sm.ncand[r], nc) : 0;
       if (nc) {
         const int gq = opaque(g);
+        const float k8q = rc_k8(), mk8q = __fmul_rn(rc_m(), k8q);
         unsigned bits = 0u;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
@@ -835,8 +845,9 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if ((bits >> (4 * (tt & 7) + i)) & 1u) {  // (the fast path holds <= 31 + CAP < CAPL keys)
-              sm.u.sel.ce[r][cpos] = scr(tt, i);
-              sm.u.sel.cj[r][cpos] = j0 + 4 * gq + i;
+              const float u = scr(tt, i);
+              sm.u.sel.ce[r][cpos] = u;
+              sm.u.sel.cj[r][cpos] = (j0 + 4 * gq + i) | (bin1(u, k8q, mk8q) << 16);  // bin beside the index
               ++cpos;
             }
           }
@@ -850,10 +861,6 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     // lane a takes entry a; the list is read back four entries at a time (broadcast loads)
     for (int row = w; row < ROWS; row += NW) {
       const int c = __builtin_amdgcn_readfirstlane(min(sm.ncand[row], CAPL));
-      {  // tag each entry with its level-1 bin (this wave alone reads and writes the row's list)
-        const float k8r = sm.r_k8[row], mk8r = __fmul_rn(sm.r_m[row], k8r);
-        for (int a = lane; a < c; a += 64) sm.u.sel.cj[row][a] |= bin1(sm.u.sel.ce[row][a], k8r, mk8r) << 16;
-      }
       const int b0 = sm.ts[row][0].valid ? (int)sm.ts[row][0].prefix : -1;
       const int b1 = (int)sm.ts[row][1].prefix, b2 = (int)sm.ts[row][2].prefix, b3 = (int)sm.ts[row][3].prefix;
       for (int a0 = 0; a0 < c; a0 += 64) {
@@ -1115,10 +1122,13 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       if (lane < nsel) {
         const float ul = sm.win_u[row][lane];
         jl = sm.win_j[row][lane];
-        for (int q = 0; q < nsel; ++q) {
-          const float uq = sm.win_u[row][q];
-          const int jq = sm.win_j[row][q];
-          rank += (uq > ul) || (uq == ul && jq < jl);
+#pragma unroll
+        for (int q = 0; q < 32; q += 4) {  // four entries per (broadcast) read, branch-free compares
+          const f32x4 u4 = *reinterpret_cast<const f32x4*>(&sm.win_u[row][q]);
+          const u32x4 j4 = *reinterpret_cast<const u32x4*>(&sm.win_j[row][q]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            rank += (int)(q + e < nsel) & ((int)(u4[e] > ul) | ((int)(u4[e] == ul) & (int)((int)j4[e] < jl)));
         }
         if (p.top32) p.top32[ri.grow * 32 + rank] = jl;
         if (rank == 0) sm.top0[row] = jl;
