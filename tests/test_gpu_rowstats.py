@@ -161,3 +161,26 @@ def test_video_full_rows_sample(kvprof_lib):
     for k in gs:
         full = g[k].reshape((2, 2340) + g[k].shape[1:])[:, sel].reshape(gs[k].shape)
         assert np.array_equal(full, gs[k]), k
+
+
+def test_video_shape_ties_and_redo(kvprof_lib):
+    """Full key count (6,240) with the selection's hard cases in one workgroup: uniform rows (every
+    key tied: the slow path refines down to key indices), rows dominated by one key (the threshold
+    keeps too few keys: the histogram is redone over all keys), rows whose boundary bins hold a block
+    of 301 identical keys, and ordinary rows."""
+    rng = np.random.default_rng(17)
+    Sk = 6240
+    k = rng.standard_normal((1, 1, Sk, 128)).astype(np.float32)
+    k[0, 0, 100:401] = k[0, 0, 7]  # 301 copies of key 7
+    q = rng.standard_normal((1, 1, 16, 128)).astype(np.float32)
+    q[0, 0, 0:4] = 0.0
+    q[0, 0, 4:8] = k[0, 0, 5000] * 3.0
+    q[0, 0, 8:12] = k[0, 0, 7] * 0.4
+    Q, K = inputs.to_bf16(q), inputs.to_bf16(k)
+    bias = inputs.video_key_bias()
+    g = _np(B.run(Q.to(DEV), K.to(DEV), want=ALL + ("region_mass", "frame_mass"), scale=128 ** -0.5,
+                  key_bias=torch.from_numpy(bias).to(DEV), **VIDEO_KW))
+    torch.cuda.synchronize()
+    ref = O.row_stats(inputs.bf16_values(Q)[0, 0], inputs.bf16_values(K)[0, 0], scale=128 ** -0.5,
+                      key_bias=bias, **VIDEO_KW)
+    P.check_rows(g, ref)
