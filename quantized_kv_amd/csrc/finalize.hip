@@ -51,17 +51,29 @@ __device__ __forceinline__ int bin100(float x, int bins) {
   return bn < 0 ? 0 : (bn >= bins ? bins - 1 : bn);
 }
 
-// One thread per row: integer atomics, so the counts are independent of the order.
-__global__ void hist_kernel(const float* __restrict__ support, const float* __restrict__ region,
-                            int n_batch, int rows_per_b, int nreg, int bins, unsigned* __restrict__ hist) {
-  long long total = (long long)n_batch * rows_per_b;
-  for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
-       t += (long long)gridDim.x * blockDim.x) {
-    long long b = t / rows_per_b;
-    unsigned* hb = hist + b * (long long)(1 + nreg) * bins;
-    atomicAdd(&hb[bin100(support[t], bins)], 1u);
-    for (int q = 0; q < nreg; ++q) atomicAdd(&hb[(1 + q) * bins + bin100(region[t * nreg + q], bins)], 1u);
+// Workgroup (record b, chunk c) counts rows [c*kHistRows, (c+1)*kHistRows) of record b into an LDS
+// histogram, then adds its nonzero bins to the record's histogram. Integer atomics only, so the
+// counts do not depend on the order.
+constexpr int kHistRows = 2048;
+constexpr int kHistMaxWords = 9 * 1024;  // (1 + KVPROF_MAX_REGIONS) histograms of <= 1024 bins
+__global__ __launch_bounds__(256) void hist_kernel(const float* __restrict__ support, const float* __restrict__ region,
+                                                   int rows_per_b, int nreg, int bins, unsigned* __restrict__ hist) {
+  __shared__ unsigned h[kHistMaxWords];
+  const int nw = (1 + nreg) * bins;
+  const int chunks = (rows_per_b + kHistRows - 1) / kHistRows;
+  const long long b = blockIdx.x / chunks;
+  for (int i = threadIdx.x; i < nw; i += blockDim.x) h[i] = 0u;
+  __syncthreads();
+  const int r0 = (int)(blockIdx.x % chunks) * kHistRows, r1 = min(rows_per_b, r0 + kHistRows);
+  for (int r = r0 + threadIdx.x; r < r1; r += blockDim.x) {
+    const long long t = b * rows_per_b + r;
+    atomicAdd(&h[bin100(support[t], bins)], 1u);
+    for (int q = 0; q < nreg; ++q) atomicAdd(&h[(1 + q) * bins + bin100(region[t * nreg + q], bins)], 1u);
   }
+  __syncthreads();
+  unsigned* hb = hist + b * (long long)nw;
+  for (int i = threadIdx.x; i < nw; i += blockDim.x)
+    if (h[i]) atomicAdd(&hb[i], h[i]);
 }
 
 __global__ void zero_u32_kernel(unsigned* p, long long n) {
@@ -155,10 +167,9 @@ hipError_t launch_hist(const float* support, const float* region_mass, int n_bat
                        int n_regions, int bins, unsigned* hist, hipStream_t s) {
   long long nh = (long long)n_batch * (1 + n_regions) * bins;
   hipLaunchKernelGGL(zero_u32_kernel, dim3(grid_for(nh, 256)), dim3(256), 0, s, hist, nh);
-  long long n = (long long)n_batch * rows_per_b;
-  if (n > 0)
-    hipLaunchKernelGGL(hist_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, support, region_mass,
-                       n_batch, rows_per_b, n_regions, bins, hist);
+  if ((long long)n_batch * rows_per_b > 0)
+    hipLaunchKernelGGL(hist_kernel, dim3((unsigned)((long long)((rows_per_b + kHistRows - 1) / kHistRows) * n_batch)),
+                       dim3(256), 0, s, support, region_mass, rows_per_b, n_regions, bins, hist);
   return hipGetLastError();
 }
 
