@@ -56,7 +56,7 @@ extern "C" {
 /* Limits of this build. */
 #define KVPROF_HEAD_DIM 128      /* row_stats / attend head dimension                               */
 #define KVPROF_MAX_KEYS 6272     /* keys per row held on chip by one workgroup (8 waves x 49 tiles)  */
-#define KVPROF_MAX_KEYS_MX 2048  /* keys per row in MXFP8 mode                                       */
+#define KVPROF_MAX_KEYS_MX 6400  /* keys per row in MXFP8 mode (8 waves x 50 tiles)                    */
 #define KVPROF_MAX_REGIONS 8
 #define KVPROF_MAX_FRAMES 64
 

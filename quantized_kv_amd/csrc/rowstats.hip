@@ -383,7 +383,7 @@ __device__ void scan_row(SM& sm, int row, int lane) {
 }
 
 template <int TPW>
-constexpr int stash_tiles() { return TPW == 49 ? 5 : 0; }
+constexpr int stash_tiles() { return TPW == 49 ? 5 : (TPW == 50 ? 6 : 0); }
 
 // One workgroup = one row block (16 rows of one (batch, KV head)). SLOW = false: the main kernel, one
 // block per workgroup; a block whose exact ranks need the slow path is appended to the redo list
@@ -1255,18 +1255,18 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     __syncthreads();
     const RowInfo me = row_info(p, b, hkv, rb, r);
     const rsrc_t rkr = make_rsrc(p.k_ref + kvh * p.n_k * KVPROF_HEAD_DIM, head_bytes);
-    u32x4 qr[4];
+    // the reference Q fragments replace this lane's (long consumed) MX Q fragments in LDS
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      qr[ks] = me.ok ? *reinterpret_cast<const u32x4*>(p.q_ref + (size_t)me.grow * KVPROF_HEAD_DIM + ks * 32 + 8 * g)
-                     : zero4();
+      sm.qs[r][ks * 4 + g] = me.ok ? *reinterpret_cast<const u32x4*>(p.q_ref + (size_t)me.grow * KVPROF_HEAD_DIM + ks * 32 + 8 * g)
+                                   : zero4();
     auto ref_tile = [&](int j0, float (&u)[4]) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int ja = j0 + r;
         u32x4 kf = __builtin_amdgcn_raw_buffer_load_b128(rkr, (unsigned)(ja * KVPROF_HEAD_DIM + ks * 32 + 8 * g) * 2u, 0, 0);
-        acc = mfma_step<KSRC_BF16>(kf, qr[ks], acc);
+        acc = mfma_step<KSRC_BF16>(kf, sm.qs[r][ks * 4 + g], acc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1431,7 +1431,7 @@ hipError_t launch_t(const RowStatsParams& p, hipStream_t s) {
 int row_stats_tpw_for(int n_k, bool mx) {
   const int need = (n_k + NW * 16 - 1) / (NW * 16);
   static const int kT[] = {1, 2, 4, 8, 16, 24, 32, 40, 49};
-  static const int kTmx[] = {2, 4, 8, 16};
+  static const int kTmx[] = {2, 4, 8, 16, 24, 32, 40, 50};  // even: 32-key P blocks never straddle waves
   if (mx) {
     for (int t : kTmx)
       if (t >= need) return t;
@@ -1449,6 +1449,10 @@ hipError_t launch_row_stats(const RowStatsParams& p, int tpw, int ksrc, bool mx,
       case 4: return launch_t<4, KSRC_BF16, true>(p, s);
       case 8: return launch_t<8, KSRC_BF16, true>(p, s);
       case 16: return launch_t<16, KSRC_BF16, true>(p, s);
+      case 24: return launch_t<24, KSRC_BF16, true>(p, s);
+      case 32: return launch_t<32, KSRC_BF16, true>(p, s);
+      case 40: return launch_t<40, KSRC_BF16, true>(p, s);
+      case 50: return launch_t<50, KSRC_BF16, true>(p, s);
       default: return hipErrorInvalidValue;
     }
   }

@@ -17,6 +17,38 @@ def _np(d):
     return {k: v.detach().cpu().numpy() for k, v in d.items() if isinstance(v, torch.Tensor)}
 
 
+def _check_zero_frac(got, p_ref, n):
+    """Zero fraction of the P path: exact count except keys whose fp32 probability sits within the
+    tie margin of the E4M3 underflow boundary (or in a block whose shared exponent is itself at a
+    boundary)."""
+    for r in range(len(got)):
+        p32 = p_ref[r].astype(np.float32).astype(np.float64)
+        lo = hi = 0
+        for b0 in range(0, n, 32):
+            blk = p32[b0:b0 + 32]
+            amax = blk.max()
+            e = O.e8m0_exponent(float(amax))
+            edge = any(abs(amax - 448 * 2.0 ** ee) <= 1e-5 * amax for ee in (e - 1, e))
+            x = blk * 2.0 ** -e
+            zero = (blk > 0) & (x <= 2.0 ** -10)
+            near = np.abs(x - 2.0 ** -10) <= 1e-5 * 2.0 ** -10
+            if edge:
+                hi += int(np.sum(blk > 0))
+            else:
+                lo += int(np.sum(zero & ~near))
+                hi += int(np.sum(zero | near))
+        cnt = int(round(got[r] * n))
+        assert lo <= cnt <= hi, (r, cnt, lo, hi)
+
+
+def _check_argmax(got, scores, name):
+    for r in range(len(got)):
+        srt = np.sort(scores[r])[::-1]
+        if abs(srt[0] - srt[1]) < P.tie_margin(srt[0], srt[1]):
+            continue
+        assert got[r] == scores[r].argmax(), (name, r)
+
+
 def test_mxfp8_tiny(kvprof_lib):
     Q, K, _ = inputs.tiny_inputs(1)
     signs = inputs.hadamard_signs(4)
@@ -39,32 +71,10 @@ def test_mxfp8_tiny(kvprof_lib):
         P.check_close("tv_qk", gv["tv_qk"], ref["tv_qk"], atol=P.MASS_ATOL)
         P.check_close("tv_p", gv["tv_p"], ref["tv_p"], atol=P.MASS_ATOL)
         P.check_close("p_rowsum", gv["p_rowsum"], ref["p_rowsum"], atol=P.MASS_ATOL)
-        # zero fraction: exact count except keys whose fp32 probability sits within the tie margin of
-        # the E4M3 underflow boundary (or in a block whose shared exponent is itself at a boundary)
-        for r in range(128):
-            p32 = ref["p"][r].astype(np.float32).astype(np.float64)
-            lo = hi = 0
-            for b0 in range(0, 128, 32):
-                blk = p32[b0:b0 + 32]
-                amax = blk.max()
-                e = O.e8m0_exponent(float(amax))
-                edge = any(abs(amax - 448 * 2.0 ** ee) <= 1e-5 * amax for ee in (e - 1, e))
-                x = blk * 2.0 ** -e
-                zero = (blk > 0) & (x <= 2.0 ** -10)
-                near = np.abs(x - 2.0 ** -10) <= 1e-5 * 2.0 ** -10
-                if edge:
-                    hi += int(np.sum(blk > 0))
-                else:
-                    lo += int(np.sum(zero & ~near))
-                    hi += int(np.sum(zero | near))
-            cnt = int(round(gv["p_zero_frac"][r] * 128))
-            assert lo <= cnt <= hi, (var, r, cnt, lo, hi)
+        _check_zero_frac(gv["p_zero_frac"], ref["p"], 128)
         for name, sc in (("argmax", ref["scores"]), ("argmax_ref", ref["ref_scores"])):
-            for r in range(128):
-                srt = np.sort(sc[r])[::-1]
-                if abs(srt[0] - srt[1]) < P.tie_margin(srt[0], srt[1]):
-                    continue
-                assert gv[name][r] == ref[name][r], (var, name, r)
+            _check_argmax(gv[name], sc, name)
+            assert np.array_equal(ref[name], sc.argmax(axis=1))  # the oracle's own argmax: lowest index
 
 
 @pytest.mark.parametrize("R", [0, 16, 64])
@@ -113,3 +123,35 @@ def test_attend_int4_decode(kvprof_lib, R):
     assert tensor_rel == pytest.approx(O.rel_l2(gq["o"].astype(np.float64), gr["o"].astype(np.float64)), rel=1e-6)
     if R == 0:
         assert 0.02 < tensor_rel < 0.3  # 4-bit K/V: error of the order of ten percent
+
+
+def test_mxfp8_video_sampled(kvprof_lib):
+    """MXFP8 mode at the video shape (6,240 keys, bias, regions, frames): two heads of sampled record
+    0 on the GPU, the oracle on 16 rows of each."""
+    rec = inputs.video_record(0, with_v=False, sampled=True)
+    heads = [0, 13]
+    Q, K = rec.q[heads][None], rec.k[heads][None]  # [1, 2, 96, 128], [1, 2, 6240, 128]
+    signs = inputs.hadamard_signs(4)
+    sg = torch.from_numpy(signs).to(DEV)
+    qd, kd = Q.to(DEV), K.to(DEV)
+    qc, qs = B.kvprof_pack_mxfp8(qd.reshape(-1, 128), sg)
+    kc, ks = B.kvprof_pack_mxfp8(kd.reshape(-1, 128), sg)
+    bias = inputs.video_key_bias()
+    kw = dict(region_bounds=inputs.VIDEO_REGION_BOUNDS, frame_len=inputs.LF_TOKENS, n_frames=inputs.N_KEY_FRAMES)
+    want = ("support", "top_mass", "top32", "strict_zero", "region_mass", "frame_mass", "tv_qk", "argmax",
+            "argmax_ref", "p_zero_frac", "tv_p", "p_rowsum")
+    g = _np(B.run(qd, kd, want=want, mode=B.MODE_MXFP8, q_codes=qc, q_scales=qs, k_codes=kc, k_scales=ks,
+                  scale=128 ** -0.5, key_bias=torch.from_numpy(bias).to(DEV), **kw))
+    torch.cuda.synchronize()
+    rows = np.r_[0:8, 88:96]
+    qv, kv = inputs.bf16_values(Q[0]), inputs.bf16_values(K[0])
+    for hi in range(2):
+        ref = O.mx_row_stats(qv[hi][rows], kv[hi], signs, scale=128 ** -0.5, key_bias=bias, **kw)
+        gv = {k: v[hi * 96:(hi + 1) * 96][rows] for k, v in g.items()}
+        P.check_rows(gv, ref)
+        P.check_close("tv_qk", gv["tv_qk"], ref["tv_qk"], atol=P.MASS_ATOL)
+        P.check_close("tv_p", gv["tv_p"], ref["tv_p"], atol=P.MASS_ATOL)
+        P.check_close("p_rowsum", gv["p_rowsum"], ref["p_rowsum"], atol=P.MASS_ATOL)
+        _check_zero_frac(gv["p_zero_frac"], ref["p"], kv.shape[1])
+        _check_argmax(gv["argmax"], ref["scores"], "argmax")
+        _check_argmax(gv["argmax_ref"], ref["ref_scores"], "argmax_ref")
