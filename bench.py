@@ -13,6 +13,9 @@ reports, inputs already resident in HBM:
 * full_rows: the same for 2,340 queries per head (one record per step by default, --records).
 * decode   : 16 query heads sharing 2 KV heads, 4,096 cached keys, last 256 positions, attention
              output over the packed 4-bit K/V (R = 16) with top-32 and recent-window mass.
+* mx_sampled: the sampled workload in MXFP8 mode: each step packs Q and K (signed-H128 + E4M3/E8M0
+             K32) and computes every statistic on the MX rows plus TV / argmax against the bf16
+             rows and the P path.
 
 Prints one JSON line (metric, value in rows/s, roofline of the row kernel, oracle CPU baseline).
 """
@@ -37,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode"])
+    ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode", "mx_sampled"])
     ap.add_argument("--records", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -193,6 +196,59 @@ def run_video(args, sampled: bool):
     return out
 
 
+def run_mx(args):
+    import torch
+
+    from quantized_kv_amd import binding as B
+    from quantized_kv_amd import inputs
+
+    dev = torch.device("cuda:0")
+    n_rec = args.records or inputs.N_RECORDS
+    Q, K = video_inputs(n_rec, True, dev)
+    Bn, H, Mq, _ = Q.shape
+    Sk = K.shape[2]
+    rows = Bn * H * Mq
+    lib = B.load()
+    signs = torch.from_numpy(inputs.hadamard_signs(4)).to(dev)
+    qc = torch.empty(Q.shape, dtype=torch.uint8, device=dev)
+    qs = torch.empty(Q.shape[:-1] + (4,), dtype=torch.uint8, device=dev)
+    kc = torch.empty(K.shape, dtype=torch.uint8, device=dev)
+    ks = torch.empty(K.shape[:-1] + (4,), dtype=torch.uint8, device=dev)
+    bias = torch.from_numpy(inputs.video_key_bias()).to(dev)
+    want = ("support", "top_mass", "top32", "strict_zero", "region_mass", "frame_mass", "tv_qk", "argmax",
+            "argmax_ref", "p_zero_frac", "tv_p", "p_rowsum")
+    res = B.run(Q, K, want=want, mode=B.MODE_MXFP8, q_codes=qc, q_scales=qs, k_codes=kc, k_scales=ks,
+                scale=128 ** -0.5, key_bias=bias, region_bounds=inputs.VIDEO_REGION_BOUNDS,
+                frame_len=inputs.LF_TOKENS, n_frames=inputs.N_KEY_FRAMES)
+    a = res["_keepalive"][0]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step():
+        B._check("kvprof_pack_mxfp8", lib.kvprof_pack_mxfp8(Q.data_ptr(), rows, 128, signs.data_ptr(),
+                                                            qc.data_ptr(), qs.data_ptr(), sp))
+        B._check("kvprof_pack_mxfp8", lib.kvprof_pack_mxfp8(K.data_ptr(), K.numel() // 128, 128, signs.data_ptr(),
+                                                            kc.data_ptr(), ks.data_ptr(), sp))
+        B.kvprof_row_stats(a, stream)
+
+    ms = time_it(step, args.steps, args.warmup, stream)
+    ms_rows = time_it(lambda: B.kvprof_row_stats(a, stream), args.steps, 1, stream)
+    # algorithmic bytes of the MX row statistics: K and Q codes + scales once, the bf16 reference K
+    # and Q once, the bias, and the outputs
+    out_row = 4 + 12 + 128 + 4 + 12 + 64 + 6 * 4
+    nbytes = K.numel() * (1 + 2) + K.numel() // 32 + Q.numel() * (1 + 2) + Q.numel() // 32 + Sk * 4 + rows * out_row
+    gbs = nbytes / (ms_rows * 1e-3) / 1e9
+    return {"metric": METRIC, "value": round(rows / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "video steady chunk, sampled queries, MXFP8 mode (pack + stats)",
+                       "records": Bn, "heads": H, "queries_per_head": Mq, "keys": Sk, "head_dim": 128,
+                       "rows_per_step": rows, "outputs": list(want)},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes},
+            "row_kernel_ms": round(ms_rows, 4)}
+
+
 def run_decode(args):
     import torch
 
@@ -237,6 +293,8 @@ def main():
         out = copy_calibration(args)
     elif args.workload == "decode":
         out = run_decode(args)
+    elif args.workload == "mx_sampled":
+        out = run_mx(args)
     else:
         out = run_video(args, sampled=args.workload == "sampled")
     print(json.dumps(out), flush=True)
