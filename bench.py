@@ -61,7 +61,7 @@ def video_inputs(n_records: int, sampled: bool, dev):
     return torch.stack(qs), torch.stack(ks)
 
 
-KERNEL_SOURCES = ("quantized_kv_amd/csrc/rowstats.hip", "quantized_kv_amd/csrc/kvprof_device.h",
+KERNEL_SOURCES = ("quantized_kv_amd/csrc/rowstats_impl.h", "quantized_kv_amd/csrc/kvprof_device.h",
                   "quantized_kv_amd/csrc/kvprof_internal.h")
 COUNTERS = os.path.join(ROOT, "profiles", "row_kernel_video_sampled_counters.json")
 

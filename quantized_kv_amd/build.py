@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvprof.so")
-SOURCES = ["codecs.hip", "rowstats.hip", "finalize.hip", "api.hip"]
+SOURCES = ["rowstats_mx.hip", "rowstats_int4.hip", "rowstats_bf16.hip", "codecs.hip", "rowstats.hip",
+           "finalize.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -45,7 +46,7 @@ def _compile(src: str, extra) -> str:
 def build(check: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     extra = ["-Rpass-analysis=kernel-resource-usage"] if check else []
-    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), max(1, os.cpu_count() or 1), 8)) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]

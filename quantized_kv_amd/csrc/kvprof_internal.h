@@ -79,6 +79,9 @@ enum KSrc { KSRC_BF16 = 0, KSRC_INT4 = 1 };
 
 // Main row kernel. tpw = 16-key tiles per wave (8 waves per workgroup, 16 rows per workgroup).
 hipError_t launch_row_stats(const RowStatsParams& p, int tpw, int ksrc, bool mx, hipStream_t s);
+hipError_t launch_row_stats_bf16(const RowStatsParams& p, int tpw, hipStream_t s);
+hipError_t launch_row_stats_int4(const RowStatsParams& p, int tpw, hipStream_t s);
+hipError_t launch_row_stats_mx(const RowStatsParams& p, int tpw, hipStream_t s);
 int row_stats_tpw_for(int n_k, bool mx);  // tiles per wave this build uses for n_k keys, or -1
 
 hipError_t launch_heatmap(const float* frame_mass, const int* row_group, int n_batch, int hq,

@@ -81,7 +81,7 @@ def _args(**over):
     (dict(q=0x10008), B.KVPROF_EALIGN, "16-byte"),
     (dict(mode=7), B.KVPROF_EINVAL, "unknown mode"),
     (dict(mode=B.MODE_MXFP8), B.KVPROF_EINVAL, "q_codes"),
-    (dict(mode=B.MODE_MXFP8, n_k=4096, q_codes=1, q_scales=1, k_codes=1, k_scales=1), B.KVPROF_EUNSUPPORTED, "exceeds"),
+    (dict(mode=B.MODE_MXFP8, n_k=6401, q_codes=1, q_scales=1, k_codes=1, k_scales=1), B.KVPROF_EUNSUPPORTED, "exceeds"),
     (dict(mode=B.MODE_INT4KV), B.KVPROF_EINVAL, "kv_packed"),
     (dict(causal=2), B.KVPROF_EINVAL, "causal"),
     (dict(q_pos0=-1), B.KVPROF_EINVAL, "q_pos0"),
