@@ -53,6 +53,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
 // Keys are ordered by (D, j): D the 32-bit order key of the score, j the key index. The group that
 // holds a target's rank is narrowed one 8-bit digit at a time, first over D (phase 0: the group is
@@ -82,8 +83,13 @@ struct Sel {
   // one 64-bit counter per bin: key count in bits 44..63, fixed-point mass (2^31 = 1) in bits 0..43,
   // so a single LDS atomic per key updates both
   unsigned long long hist[ROWS][HB];
-  float ce[ROWS][CAPL];  // candidate scores u
-  int cj[ROWS][CAPL];    // candidate key index (fast path: | level-1 bin << 16)
+  union {
+    struct {
+      float ce[ROWS][CAPL];  // slow path: candidate scores u
+      int cj[ROWS][CAPL];    // slow path: candidate key index
+    };
+    unsigned long long ck[ROWS][CAPL];  // fast path: rank keys (rank_key)
+  };
   union {
     float sorted_e[ROWS][CAP];  // slow path: candidate e' by rank
     int crank[ROWS][CAPL];      // fast path: rank of a candidate inside its level-1 bin
@@ -200,6 +206,20 @@ __device__ __forceinline__ unsigned dkey32(float u, float k32, float mk32) {
 }
 // Fixed-point mass of a key: trunc(e') <= 2^31 (an error below 2^-31 of the largest key's weight).
 __device__ __forceinline__ unsigned fixmass(float e) { return (unsigned)e; }
+
+// Rank key of a gathered key: level-1 bin (bits 48..55), then the score descending (its bits mapped
+// to an increasing unsigned order, complemented: bits 16..47), then the key index (bits 0..15). Keys
+// of one bin are contiguous and ordered as the ranks are defined (score descending, index
+// ascending), so a rank inside the bin is a count of smaller keys minus the keys of earlier bins.
+__device__ __forceinline__ unsigned long long rank_key(float u, int j, int bin) {
+  const unsigned b = __float_as_uint(u);
+  const unsigned ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)bin << 48) | ((unsigned long long)(~ord) << 16) | (unsigned)j;
+}
+__device__ __forceinline__ float rank_key_score(unsigned long long k) {
+  const unsigned ord = ~(unsigned)(k >> 16);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
 constexpr int kSh = 24;  // level-1 bin = key >> 24
 
 __device__ __forceinline__ int remap_block(int bid, int n) {
@@ -848,8 +868,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           for (int i = 0; i < 4; ++i) {
             if ((bits >> (4 * (tt & 7) + i)) & 1u) {  // (the fast path holds <= 31 + CAP < CAPL keys)
               const float u = scr(tt, i);
-              sm.u.sel.ce[r][cpos] = u;
-              sm.u.sel.cj[r][cpos] = (j0 + 4 * gq + i) | (bin1(u, k8q, mk8q) << 16);  // bin beside the index
+              sm.u.sel.ck[r][cpos] = rank_key(u, j0 + 4 * gq + i, bin1(u, k8q, mk8q));
               ++cpos;
             }
           }
@@ -860,30 +879,28 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     }
     __syncthreads();
     // rank every boundary-bin key inside its bin (the other keys of the bins above bq0 need none):
-    // lane a takes entry a; the list is read back four entries at a time (broadcast loads)
+    // lane a takes entry a and counts the smaller rank keys of the list, and those of earlier bins.
+    // The wave that owns the row pads the list to a multiple of 4 with the largest key first.
     for (int row = w; row < ROWS; row += NW) {
       const int c = __builtin_amdgcn_readfirstlane(min(sm.ncand[row], CAPL));
+      const int c4 = (c + 3) & ~3;
+      if (c + lane < c4) sm.u.sel.ck[row][c + lane] = ~0ull;
       const int b0 = sm.ts[row][0].valid ? (int)sm.ts[row][0].prefix : -1;
       const int b1 = (int)sm.ts[row][1].prefix, b2 = (int)sm.ts[row][2].prefix, b3 = (int)sm.ts[row][3].prefix;
       for (int a0 = 0; a0 < c; a0 += 64) {
         const int a = a0 + lane;
-        const float ua = a < c ? sm.u.sel.ce[row][a] : 0.f;
-        const int ca = a < c ? sm.u.sel.cj[row][a] : -1;
-        const int ba = ca >> 16;
-        int rank = 0;
+        const unsigned long long ka = a < c ? sm.u.sel.ck[row][a] : 0ull;
+        const unsigned long long k0 = ka & ~((1ull << 48) - 1);  // first key of a's bin
+        int below = 0, earlier = 0;
 #pragma unroll 4
-        for (int q = 0; q < c; q += 4) {
-          const f32x4 u4 = *reinterpret_cast<const f32x4*>(&sm.u.sel.ce[row][q]);
-          const u32x4 c4 = *reinterpret_cast<const u32x4*>(&sm.u.sel.cj[row][q]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // bitwise, not short-circuit: no branches in the loop
-            const int cq = (int)c4[e];
-            rank += (int)(q + e < c) & (int)((cq >> 16) == ba) & ((int)(u4[e] > ua) | ((int)(u4[e] == ua) & (int)(cq < ca)));
-          }
+        for (int q = 0; q < c4; q += 2) {
+          const u64x2 k2 = *reinterpret_cast<const u64x2*>(&sm.u.sel.ck[row][q]);
+          below += (int)(k2[0] < ka) + (int)(k2[1] < ka);
+          earlier += (int)(k2[0] < k0) + (int)(k2[1] < k0);
         }
+        const int ba = (int)(ka >> 48);
         const bool need = ba >= b0 || ba == b1 || ba == b2 || ba == b3;
-        if (a < c) sm.u.sel.crank[row][a] = need ? rank : 0;
+        if (a < c) sm.u.sel.crank[row][a] = need ? below - earlier : 0;
       }
     }
     __syncthreads();
@@ -894,16 +911,17 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       const int b0 = sm.ts[row][0].valid ? (int)sm.ts[row][0].prefix : -1;
       unsigned long long acc[NT] = {0ull, 0ull, 0ull, 0ull};
       for (int a = lane; a < c; a += 64) {
-        const float ua = sm.u.sel.ce[row][a];
-        const int ca = sm.u.sel.cj[row][a];
-        const unsigned dga = (unsigned)(ca >> 16);
+        const unsigned long long ka = sm.u.sel.ck[row][a];
+        const float ua = rank_key_score(ka);
+        const int ja = (int)(ka & 0xFFFFu);
+        const unsigned dga = (unsigned)(ka >> 48);
         const int rk = sm.u.sel.crank[row][a];
         if ((int)dga < b0) {  // ranked above the top-32 boundary bin: one of the 32
           const int slot = atomicAdd(&sm.nwin[row], 1);
           sm.win_u[row][slot] = ua;
-          sm.win_j[row][slot] = ca & 0xFFFF;
+          sm.win_j[row][slot] = ja;
         }
-        const float ea = __builtin_amdgcn_exp2f(fmaxf(ua + (kOff - mr), -256.f));
+      const float ea = __builtin_amdgcn_exp2f(fmaxf(ua + (kOff - mr), -256.f));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const TState& ts = sm.ts[row][t];
@@ -912,7 +930,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           if (t == 0) {
             if (rk <= rr) {  // ranks 0..target of the top-32 list
               sm.win_u[row][ts.cnt_before + rk] = ua;
-              sm.win_j[row][ts.cnt_before + rk] = ca & 0xFFFF;
+              sm.win_j[row][ts.cnt_before + rk] = ja;
             }
           } else {
             if (rk < rr) acc[t] += fixmass(ea);
