@@ -487,12 +487,12 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   // tile's 16 bias values. The compiler does not track these writes, so the wait before reading a
   // slot is explicit: loads retire in issue order, and the 5 (kRing - 1) loads of the later tiles
   // may still be outstanding.
-  auto issue = [&](int t) {
+  auto issue_from = [&](rsrc_t src, int t) {
     const int slot = t % kRing;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kt = 4 * ks + (lane >> 4);  // key inside the tile
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)&sm.u.a.ring[w][slot][ks][0], 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)&sm.u.a.ring[w][slot][ks][0], 16,
                                                (unsigned)((kbase + t * 16 + kt) * (KVPROF_HEAD_DIM * 2) + (((lane & 15) ^ kt) * 16)),
                                                0, 0, 0);
     }
@@ -500,6 +500,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (__attribute__((address_space(3))) void*)&sm.u.a.rbias[w][slot][0], 4,
                                                (unsigned)(kbase + t * 16 + lane) * 4u, 0, 0, 0);
   };
+  auto issue = [&](int t) { issue_from(rk, t); };
   if (KSRC == KSRC_BF16) {
 #pragma unroll
     for (int t = 0; t < kRing - 1 && t < TPW; ++t) issue(t);
@@ -1280,83 +1281,100 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     for (int ks = 0; ks < 4; ++ks)
       sm.qs[r][ks * 4 + g] = me.ok ? *reinterpret_cast<const u32x4*>(p.q_ref + (size_t)me.grow * KVPROF_HEAD_DIM + ks * 32 + 8 * g)
                                    : zero4();
-    auto ref_tile = [&](int j0, float (&u)[4]) {
+    // Reference scores of tile t through the same LDS load ring as the MX scores (whole keys per
+    // load, swizzled rows); the caller has issued tile t, and this issues tile t + 1 first.
+    auto ref_tile = [&](int t, float (&u)[4]) {
+      const int j0 = kbase + t * 16;
+      if (t + 1 < TPW) {
+        issue_from(rkr, t + 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (5 * (kRing - 1)));
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (j0 < kmax) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int ja = j0 + r;
-        u32x4 kf = __builtin_amdgcn_raw_buffer_load_b128(rkr, (unsigned)(ja * KVPROF_HEAD_DIM + ks * 32 + 8 * g) * 2u, 0, 0);
-        acc = mfma_step<KSRC_BF16>(kf, sm.qs[r][ks * 4 + g], acc);
+        for (int ks = 0; ks < 4; ++ks)
+          acc = mfma_step<KSRC_BF16>(sm.u.a.ring[w][t % kRing][r >> 2][(r & 3) * 16 + ((4 * ks + g) ^ r)],
+                                     sm.qs[r][ks * 4 + g], acc);
+      }
+      const f32x4 bias = *reinterpret_cast<const f32x4*>(&sm.u.a.rbias[w][t % kRing][4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + 4 * g + i;
+        u[i] = j < nvis ? fmaf(acc[i], p.scale_log2, fmaxf(bias[i] * kLog2e, kNegBig)) : -INFINITY;
+      }
+    };
+    // The same reference tile with direct loads (for the unrolled pass below, which the ring's
+    // prefetch chain would cost registers in).
+    auto ref_tile_direct = [&](int j0, float (&u)[4]) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (j0 < kmax) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x4 kf = __builtin_amdgcn_raw_buffer_load_b128(rkr, (unsigned)((j0 + r) * KVPROF_HEAD_DIM + ks * 32 + 8 * g) * 2u, 0, 0);
+          acc = mfma_step<KSRC_BF16>(kf, sm.qs[r][ks * 4 + g], acc);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = j0 + 4 * g + i;
-        float bb = (p.key_bias && j < p.n_k) ? fmaxf(p.key_bias[j] * kLog2e, kNegBig) : 0.f;
-        u[i] = j < nvis ? fmaf(acc[i], p.scale_log2, bb) : -INFINITY;
+        const float bb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, (unsigned)j * 4u, 0, 0));
+        u[i] = j < nvis ? fmaf(acc[i], p.scale_log2, fmaxf(bb * kLog2e, kNegBig)) : -INFINITY;
       }
     };
-    // R1: reference max and argmax (ties to the lowest index)
-    float best = -INFINITY;
+    // R1: reference max, argmax (ties to the lowest index) and normaliser in one pass: the running
+    // sum is rescaled whenever the running max grows
+    float best = -INFINITY, zr = 0.f;
     int bestj = 0x7fffffff;
+    issue_from(rkr, 0);
 #pragma unroll 1
     for (int t = 0; t < TPW; ++t) {
       const int j0 = kbase + t * 16;
-      if (j0 >= kmax) break;
       float u[4];
-      ref_tile(j0, u);
+      ref_tile(t, u);
+      float nb_ = best;  // the running max, updated key by key together with its index
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = j0 + 4 * g + i;
-        if (u[i] > best || (u[i] == best && j < bestj)) {
-          best = u[i];
+        if (u[i] > nb_ || (u[i] == nb_ && j < bestj)) {
+          nb_ = u[i];
           bestj = j;
         }
       }
+      if (nb_ > -INFINITY) {
+        zr *= __builtin_amdgcn_exp2f(best - nb_);  // (0 while best is -inf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zr += __builtin_amdgcn_exp2f(u[i] - nb_);
+      }
+      best = nb_;
       __builtin_amdgcn_sched_barrier(0);
     }
+    // merge (max, argmax, sum) over the row's 4 lanes, then over the waves, in a fixed order
+    auto merge = [](float& m1, int& j1, float& z1, float m2, int j2, float z2) {
+      const float mm = fmaxf(m1, m2);
+      const float za = m1 > -INFINITY ? z1 * __builtin_amdgcn_exp2f(m1 - mm) : 0.f;
+      const float zb = m2 > -INFINITY ? z2 * __builtin_amdgcn_exp2f(m2 - mm) : 0.f;
+      if (m2 > m1 || (m2 == m1 && j2 < j1)) j1 = j2;
+      m1 = mm;
+      z1 = za + zb;
+    };
 #pragma unroll
     for (int o = 16; o <= 32; o <<= 1) {
-      float ob = __shfl_xor(best, o);
-      int oj = __shfl_xor(bestj, o);
-      if (ob > best || (ob == best && oj < bestj)) {
-        best = ob;
-        bestj = oj;
-      }
+      const float ob = __shfl_xor(best, o), oz = __shfl_xor(zr, o);
+      const int oj = __shfl_xor(bestj, o);
+      merge(best, bestj, zr, ob, oj, oz);
     }
     if (g == 0) {
       sm.red_a[w][r] = best;
       sm.red_i[w][r] = bestj;
+      sm.red_b[w][r] = zr;
     }
     __syncthreads();
-    float mref = -INFINITY;
+    float mref = -INFINITY, Zr = 0.f;
     int aref = 0x7fffffff;
-    for (int ww = 0; ww < NW; ++ww) {
-      float ob = sm.red_a[ww][r];
-      int oj = sm.red_i[ww][r];
-      if (ob > mref || (ob == mref && oj < aref)) {
-        mref = ob;
-        aref = oj;
-      }
-    }
+    for (int ww = 0; ww < NW; ++ww) merge(mref, aref, Zr, sm.red_a[ww][r], sm.red_i[ww][r], sm.red_b[ww][r]);
     if (!me.ok) mref = 0.f;
-    __syncthreads();
-    // R2: reference normaliser
-    float zr = 0.f;
-#pragma unroll 1
-    for (int t = 0; t < TPW; ++t) {
-      const int j0 = kbase + t * 16;
-      if (j0 >= kmax) break;
-      float u[4];
-      ref_tile(j0, u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) zr += __builtin_amdgcn_exp2f(u[i] - mref);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    zr = row_sum4(zr);
-    if (g == 0) sm.red_b[w][r] = zr;
-    __syncthreads();
-    float Zr = 0.f;
-    for (int ww = 0; ww < NW; ++ww) Zr += sm.red_b[ww][r];
     const float invZr = me.ok ? 1.f / Zr : 0.f;
     __syncthreads();
     // R3: TV between the MX row and the reference row, and the P path
@@ -1369,7 +1387,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         float u[4];
-        ref_tile(j0 + 16 * h2, u);
+        ref_tile_direct(j0 + 16 * h2, u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float pm = __builtin_amdgcn_exp2f(fmaxf(scr(t + h2, i) + (kOff - rc_m()), -256.f)) / rc_z();
