@@ -1,6 +1,6 @@
 """Benchmark of the KV-cache attention row profiler on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload sampled|full_rows|decode] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload sampled|full_rows|decode|decode_batch|mx_sampled] [--no-cpu-baseline]
     python bench.py --copy-calibration     # 1 GiB device copy, for scaling the HBM byte counters
 
 A step is one kvprof_row_stats call over the whole workload with every statistic the workload
@@ -13,6 +13,9 @@ reports, inputs already resident in HBM:
 * full_rows: the same for 2,340 queries per head (one record per step by default, --records).
 * decode   : 16 query heads sharing 2 KV heads, 4,096 cached keys, last 256 positions, attention
              output over the packed 4-bit K/V (R = 16) with top-32 and recent-window mass.
+* decode_batch: one decode step for 512 sequences (seeds 5000 + b): each sequence's last position,
+             16 query heads over its own 2 packed 4-bit KV heads of 4,096 keys (R = 16); the same
+             outputs. Every packed byte is read once per step.
 * mx_sampled: the sampled workload in MXFP8 mode: each step packs Q and K (signed-H128 + E4M3/E8M0
              K32) and computes every statistic on the MX rows plus TV / argmax against the bf16
              rows and the P path.
@@ -40,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode", "mx_sampled"])
+    ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode", "decode_batch", "mx_sampled"])
     ap.add_argument("--records", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -278,6 +281,69 @@ def run_decode(args):
                          "frac": round(tfs / BF16_PEAK_TFLOPS, 5), "traffic": None}}
 
 
+DECODE_BATCH = 512  # sequences per launch, seeds 5000 + b
+DECODE_BATCH_SEED0 = 5000
+
+
+def decode_batch_inputs(n_seq: int, r_window: int, dev):
+    """n_seq independent sequences, each one query position (the last, t = L - 1) for 16 query heads
+    over 2 KV heads of L keys, seeds DECODE_BATCH_SEED0 + b. K/V are packed on the device in chunks,
+    so the bf16 cache never has to be resident whole. Returns Q [n_seq, 16, 1, 128] and the blobs
+    [n_seq * 2, blob_bytes]."""
+    import torch
+
+    from quantized_kv_amd import binding as B
+    from quantized_kv_amd import inputs
+
+    L, hkv, hq = inputs.DECODE_L, inputs.DECODE_HKV, inputs.DECODE_HQ
+    blob = B.kvprof_int4kv_bytes(L, 128, r_window)
+    packed = torch.empty((n_seq * hkv, blob), dtype=torch.uint8, device=dev)
+    Q = torch.empty((n_seq, hq, 1, 128), dtype=torch.bfloat16, device=dev)
+    chunk = 32
+    for c0 in range(0, n_seq, chunk):
+        seqs = range(c0, min(n_seq, c0 + chunk))
+        qs, ks, vs = zip(*[inputs.decode_inputs(DECODE_BATCH_SEED0 + b, mq=1) for b in seqs])
+        Q[c0:c0 + len(seqs)] = torch.stack(qs).to(dev)
+        k = torch.cat(ks).to(dev)
+        v = torch.cat(vs).to(dev)
+        packed[c0 * hkv:(c0 + len(seqs)) * hkv] = B.kvprof_pack_int4kv(k, v, r_window)
+    return Q, packed
+
+
+def run_decode_batch(args):
+    """Decode-shaped attention over the packed 4-bit cache: one query position per sequence, many
+    sequences per launch, so every byte of the packed K/V is read once per step (HBM-bound)."""
+    import torch
+
+    from quantized_kv_amd import binding as B
+    from quantized_kv_amd import inputs
+
+    dev = torch.device("cuda:0")
+    L, R = inputs.DECODE_L, 16
+    n_seq = args.records or DECODE_BATCH
+    t_gen = time.time()
+    Q, packed = decode_batch_inputs(n_seq, R, dev)
+    gen_s = time.time() - t_gen
+    stream = torch.cuda.current_stream()
+    res = B.run(Q, None, want=("top32", "o", "region_mass"), attend=True, mode=B.MODE_INT4KV, kv_packed=packed,
+                r_window=R, n_k=L, n_heads_kv=inputs.DECODE_HKV, causal=True, q_pos0=L - 1,
+                region_bounds=[0, L - R, L])
+    a = res["_keepalive"][0]
+    ms = time_it(lambda: B.kvprof_attend(a, stream), args.steps, args.warmup, stream)
+    rows = Q.shape[0] * Q.shape[1]
+    # algorithmic bytes: every packed blob once, the Q rows, and the outputs (O, top-32, 2 region masses)
+    nbytes = packed.numel() + Q.numel() * 2 + rows * (128 * 4 + 32 * 4 + 2 * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": METRIC, "value": round(rows / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+            "config": {"workload": "batched decode step over 4-bit KV, R=16", "sequences": n_seq,
+                       "q_heads": inputs.DECODE_HQ, "kv_heads": inputs.DECODE_HKV, "keys": L, "positions": 1},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes},
+            "input_gen_s": round(gen_s, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -293,6 +359,8 @@ def main():
         out = copy_calibration(args)
     elif args.workload == "decode":
         out = run_decode(args)
+    elif args.workload == "decode_batch":
+        out = run_decode_batch(args)
     elif args.workload == "mx_sampled":
         out = run_mx(args)
     else:

@@ -36,6 +36,7 @@ constexpr int HB = 257;  // padded histogram stride (rows land in different LDS 
 constexpr int CAP = 256; // candidate slots per row (boundary bins)
 constexpr int CAPL = CAP + 32;   // fast-path list: the boundary bins plus the keys ranked above them
 constexpr int kRedoGrid = 256;  // workgroups of the redo kernel (they loop over the redo list)
+constexpr int kVstStride = 10;  // 32-bit words per staged V channel row: 16 keys (f16) + 2 words of padding
 constexpr float kOff = 31.f;    // e' = 2^(u - max + kOff): the largest key weighs 2^31
 constexpr int NT = 4;    // selected ranks per row
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -123,6 +124,7 @@ struct Smem {
   union {
     Sel sel;
     float ored[NW / 2][ROWS][64];
+    _Float16 vst[NW][64][2 * kVstStride];  // P.V: per wave, 64 channels x 16 keys of V (f16), padded
     struct {
       u32x4 ring[NW][kRing][4][64];  // per wave: kRing K tiles x 4 k-steps x 64 lanes (A fragments)
       float rbias[NW][kRing][16];    // the tiles' raw key bias
@@ -299,23 +301,31 @@ __device__ __forceinline__ u32x4 load_k(const RowStatsParams& p, rsrc_t rk, cons
   }
 }
 
-// V value (key j, dim c) as f16 for the P.V product (branchless for int4, as above).
+// V values of key j, channels c0 .. c0+7 (c0 a multiple of 8), as f16 for the P.V product: one
+// 16-byte load for bf16; for int4 one word of codes and one of (scale, min), with the float32 window
+// selected branchlessly as in load_k. Keys past n_k read zeros.
 template <int KSRC>
-__device__ __forceinline__ _Float16 load_v(const RowStatsParams& p, rsrc_t rv, const Int4Layout& L, int j, int c) {
+__device__ __forceinline__ void load_v8(const RowStatsParams& p, rsrc_t rv, const Int4Layout& L, int j, int c0,
+                                        _Float16 (&x)[8]) {
   if (KSRC == KSRC_BF16) {
-    const uint32_t b = __builtin_amdgcn_raw_buffer_load_b16(rv, (unsigned)(j * KVPROF_HEAD_DIM + c) * 2u, 0, 0);
-    return (_Float16)__uint_as_float(b << 16);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rv, (unsigned)(j * KVPROF_HEAD_DIM + c0) * 2u, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (_Float16)__uint_as_float(((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16);
   } else {
     const bool quant = j < (int)L.n;
     const int jq = quant ? j : 0;
-    const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(rv, (unsigned)(L.vc + (size_t)jq * 64 + c / 2), 0, 0);
-    const uint32_t wd = __builtin_amdgcn_raw_buffer_load_b32(rv, (unsigned)(L.vm + ((size_t)jq * 4 + c / 32) * 4), 0, 0);
-    const unsigned ro = (quant || j >= p.n_k) ? kOOR : (unsigned)(L.vr + ((size_t)(j - (int)L.n) * 128 + c) * 4);
-    const uint32_t f = __builtin_amdgcn_raw_buffer_load_b32(rv, ro, 0, 0);
-    const uint32_t code = (byte >> ((c & 1) * 4)) & 0xF;
+    const uint32_t codes = __builtin_amdgcn_raw_buffer_load_b32(rv, (unsigned)(L.vc + (size_t)jq * 64 + c0 / 2), 0, 0);
+    const uint32_t wd = __builtin_amdgcn_raw_buffer_load_b32(rv, (unsigned)(L.vm + ((size_t)jq * 4 + c0 / 32) * 4), 0, 0);
+    const unsigned ro = (quant || j >= p.n_k) ? kOOR : (unsigned)(L.vr + ((size_t)(j - (int)L.n) * 128 + c0) * 4);
+    const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ro, 0, 0));
+    const f32x4 bb = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ro + 16u, 0, 0));
     const float s_ = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xFFFF));
     const float m_ = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
-    return (_Float16)(quant ? fmaf((float)code, s_, m_) : __uint_as_float(f));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float rv_ = e < 4 ? a[e] : bb[e - 4];
+      x[e] = (_Float16)(quant ? fmaf((float)((codes >> (4 * e)) & 0xF), s_, m_) : rv_);
+    }
   }
 }
 
@@ -411,7 +421,7 @@ constexpr int stash_tiles() { return TPW == 49 ? 5 : (TPW == 50 ? 6 : 0); }
 // block per workgroup; a block whose exact ranks need the slow path is appended to the redo list
 // (p.redo) and finished by the SLOW = true kernel, which loops over that list and compiles the slow
 // path (its code would otherwise raise the register peak of the common case).
-template <int TPW, int KSRC, bool MX, bool SLOW>
+template <int TPW, int KSRC, bool MX, bool SLOW, bool WO>
 __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   constexpr int NL = stash_tiles<TPW>();
   __shared__ Smem<NL> sm;
@@ -1213,12 +1223,19 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   }
 
   // ---- O = P.V --------------------------------------------------------------------------------------
-  if (p.o) {
+  // V tiles pass through LDS, transposed: lane (kp, q8) loads keys 2kp and 2kp + 1, channels
+  // 8 q8 .. 8 q8 + 7 of the half with wide loads and stores them channel-major (keys contiguous);
+  // the B fragment of the MFMA (four consecutive keys of one channel) is then one 8-byte read. The
+  // staging area of a wave is written and read by that wave only (LDS operations of a wave complete
+  // in order).
+  if (WO) {  // (compiled only into the kernels launched with p.o set: its registers stay out of the others)
+    __syncthreads();  // the staging area overlays LDS that phase E read
     const float pmul = kPScale / rc_z();
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
       const float pm = opaque(pmul), offq = opaque(kOff - rc_m());  // recomputed per half, not hoisted per tile
-      const int rq = opaque(r), gq = opaque(g);  // likewise the per-key V offsets
+      const int rq = opaque(r), gq = opaque(g);
+      const int kp = opaque(lane & 7), q8 = opaque(lane >> 3);
       f32x4 oacc[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1226,21 +1243,29 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       for (int t = 0; t < TPW; ++t) {
         const int j0 = kbase + t * 16;
         if (j0 < kmax) {
-        f16x4 pa;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pa[i] = (_Float16)(__builtin_amdgcn_exp2f(fmaxf(scr(t, i) + offq, -256.f)) * pm);
+          for (int kk = 0; kk < 2; ++kk) {  // one key at a time (the scores are live in registers)
+            _Float16 x[8];
+            load_v8<KSRC>(p, rv, L, j0 + 2 * kp + kk, half * 64 + 8 * q8, x);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int c = half * 64 + db * 16 + rq;
-          f16x4 vb;
+            for (int e = 0; e < 8; ++e) sm.u.vst[w][8 * q8 + e][2 * kp + kk] = x[e];
+          }
+          f16x4 pa;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) vb[i] = load_v<KSRC>(p, rv, L, j0 + 4 * gq + i, c);
-          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, oacc[db], 0, 0, 0);
-        }
+          for (int i = 0; i < 4; ++i) pa[i] = (_Float16)(__builtin_amdgcn_exp2f(fmaxf(scr(t, i) + offq, -256.f)) * pm);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const uint2 vw = *reinterpret_cast<const uint2*>(&sm.u.vst[w][db * 16 + rq][4 * gq]);
+            const f16x4 vb = __builtin_bit_cast(f16x4, vw);
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, oacc[db], 0, 0, 0);
+          }
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // fixed-order tree over the 16 waves
+      __syncthreads();  // every wave is done with its staging area (the reduction below overlays it)
+      // fixed-order tree over the waves
       for (int s = NW / 2; s >= 1; s >>= 1) {
         if (w >= s && w < 2 * s) {
 #pragma unroll
@@ -1453,15 +1478,21 @@ __global__ void redo_reset(unsigned* redo) {
   if (threadIdx.x == 0) redo[0] = 0u;
 }
 
+template <int TPW, int KSRC, bool MX, bool WO>
+hipError_t launch_wo(const RowStatsParams& p, long long nwg, hipStream_t s) {
+  hipLaunchKernelGGL(redo_reset, dim3(1), dim3(64), 0, s, p.redo);
+  hipLaunchKernelGGL((row_kernel<TPW, KSRC, MX, false, WO>), dim3((unsigned)nwg), dim3(WGT), 0, s, p);
+  hipLaunchKernelGGL((row_kernel<TPW, KSRC, MX, true, WO>), dim3((unsigned)(nwg < kRedoGrid ? nwg : kRedoGrid)),
+                     dim3(WGT), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int TPW, int KSRC, bool MX>
 hipError_t launch_t(const RowStatsParams& p, hipStream_t s) {
   const int nrb = (p.rows_per_kv + ROWS - 1) / ROWS;
   const long long nwg = (long long)p.n_batch * p.n_heads_kv * nrb;
   if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL(redo_reset, dim3(1), dim3(64), 0, s, p.redo);
-  hipLaunchKernelGGL((row_kernel<TPW, KSRC, MX, false>), dim3((unsigned)nwg), dim3(WGT), 0, s, p);
-  hipLaunchKernelGGL((row_kernel<TPW, KSRC, MX, true>), dim3((unsigned)(nwg < kRedoGrid ? nwg : kRedoGrid)), dim3(WGT), 0, s, p);
-  return hipGetLastError();
+  return p.o ? launch_wo<TPW, KSRC, MX, true>(p, nwg, s) : launch_wo<TPW, KSRC, MX, false>(p, nwg, s);
 }
 
 }  // namespace

@@ -155,3 +155,32 @@ def test_mxfp8_video_sampled(kvprof_lib):
         _check_zero_frac(gv["p_zero_frac"], ref["p"], kv.shape[1])
         _check_argmax(gv["argmax"], ref["scores"], "argmax")
         _check_argmax(gv["argmax_ref"], ref["ref_scores"], "argmax_ref")
+
+
+def test_attend_int4_decode_batch(kvprof_lib):
+    """Several sequences in one launch, one query position each (the decode step): batch b reads
+    only its own packed KV heads."""
+    import bench
+
+    R, L = 16, inputs.DECODE_L
+    n_seq = 3
+    Q, packed = bench.decode_batch_inputs(n_seq, R, DEV)
+    rb = [0, L - R, L]
+    g = _np(B.run(Q, None, want=("top32", "o", "region_mass"), attend=True, mode=B.MODE_INT4KV,
+                  kv_packed=packed, r_window=R, n_k=L, n_heads_kv=2, causal=True, q_pos0=L - 1, region_bounds=rb))
+    torch.cuda.synchronize()
+    for s in range(n_seq):
+        q, k, v = inputs.decode_inputs(bench.DECODE_BATCH_SEED0 + s, mq=1)
+        qv = inputs.bf16_values(q)
+        for hk in range(2):
+            blob = O.pack_int4kv(inputs.bf16_values(k[hk]), inputs.bf16_values(v[hk]), R)
+            assert np.array_equal(blob, packed[2 * s + hk].cpu().numpy())
+            khat, vhat = O.unpack_int4kv(blob)
+            for h in range(8 * hk, 8 * hk + 8):
+                print(f"decode batch seq {s} head {h}", flush=True)
+                ref = O.row_stats(qv[h], khat, scale=128 ** -0.5, causal=True, q_pos0=L - 1, region_bounds=rb,
+                                  v=vhat)
+                sl = slice(s * 16 + h, s * 16 + h + 1)
+                P.check_top32(g["top32"][sl], ref["scores"], ref["n_visible"])
+                P.check_o(g["o"][sl], ref["o"])
+                P.check_close("recent mass", g["region_mass"][sl, 1], ref["region_mass"][:, 1], atol=P.MASS_ATOL)
