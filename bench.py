@@ -330,6 +330,11 @@ def run_decode_batch(args):
                 region_bounds=[0, L - R, L])
     a = res["_keepalive"][0]
     ms = time_it(lambda: B.kvprof_attend(a, stream), args.steps, args.warmup, stream)
+    # the codec on its own: pack 32 sequences' K/V (bf16 in, blobs out)
+    ks, vs = zip(*[inputs.decode_inputs(DECODE_BATCH_SEED0 + b, mq=1)[1:] for b in range(32)])
+    kc, vc = torch.cat(ks).to(dev), torch.cat(vs).to(dev)
+    ms_pack = time_it(lambda: B.kvprof_pack_int4kv(kc, vc, R), args.steps, args.warmup, stream)
+    pack_bytes = kc.numel() * 2 * 2 + kc.shape[0] * B.kvprof_int4kv_bytes(L, 128, R)
     rows = Q.shape[0] * Q.shape[1]
     # algorithmic bytes: every packed blob once, the Q rows, and the outputs (O, top-32, 2 region masses)
     nbytes = packed.numel() + Q.numel() * 2 + rows * (128 * 4 + 32 * 4 + 2 * 4)
@@ -341,6 +346,9 @@ def run_decode_batch(args):
                        "q_heads": inputs.DECODE_HQ, "kv_heads": inputs.DECODE_HKV, "keys": L, "positions": 1},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes},
+            "pack_int4kv": {"kv_heads": kc.shape[0], "ms": round(ms_pack, 4),
+                            "gbs": round(pack_bytes / (ms_pack * 1e-3) / 1e9, 1),
+                            "frac": round(pack_bytes / (ms_pack * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
             "input_gen_s": round(gen_s, 1)}
 
 
