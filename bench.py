@@ -1,6 +1,6 @@
 """Benchmark of the KV-cache attention row profiler on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload sampled|full_rows|decode|decode_batch|mx_sampled] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload sampled|full_rows|decode|decode_batch|mx_sampled|tiny] [--no-cpu-baseline]
     python bench.py --copy-calibration     # 1 GiB device copy, for scaling the HBM byte counters
 
 A step is one kvprof_row_stats call over the whole workload with every statistic the workload
@@ -19,6 +19,10 @@ reports, inputs already resident in HBM:
 * mx_sampled: the sampled workload in MXFP8 mode: each step packs Q and K (signed-H128 + E4M3/E8M0
              K32) and computes every statistic on the MX rows plus TV / argmax against the bf16
              rows and the P path.
+
+* tiny     : the three 128 x 128 variants (clean, early_focus, recent_focus) with every statistic and
+             O in one call, and the same rows in MXFP8 mode (pack + statistics): launch-latency-bound,
+             reported as microseconds per call with no roofline claim.
 
 Prints one JSON line (metric, value in rows/s, roofline of the row kernel, oracle CPU baseline).
 """
@@ -43,7 +47,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode", "decode_batch", "mx_sampled"])
+    ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode", "decode_batch", "mx_sampled", "tiny"])
     ap.add_argument("--records", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -281,6 +285,48 @@ def run_decode(args):
                          "frac": round(tfs / BF16_PEAK_TFLOPS, 5), "traffic": None}}
 
 
+def run_tiny(args):
+    """The tiny three-variant workload: latency per call (bf16 mode with O; MXFP8 mode with packing)."""
+    import torch
+
+    from quantized_kv_amd import binding as B
+    from quantized_kv_amd import inputs
+
+    dev = torch.device("cuda:0")
+    Q, K, V = (x.to(dev) for x in inputs.tiny_inputs(1))
+    rb = [0, inputs.TINY_EARLY, inputs.TINY_N]
+    stream = torch.cuda.current_stream()
+    want = ("support", "top_mass", "top32", "strict_zero", "region_mass", "row_max", "row_lse", "o")
+    a = B.run(Q, K, V, want=want, attend=True, region_bounds=rb)["_keepalive"][0]
+    ms = time_it(lambda: B.kvprof_attend(a, stream), args.steps, args.warmup, stream)
+    sg = torch.from_numpy(inputs.hadamard_signs(4)).to(dev)
+    qc, qs = B.kvprof_pack_mxfp8(Q.reshape(-1, 128), sg)
+    kc, ks = B.kvprof_pack_mxfp8(K.reshape(-1, 128), sg)
+    want_mx = ("support", "top_mass", "top32", "strict_zero", "region_mass", "tv_qk", "argmax", "argmax_ref",
+               "p_zero_frac", "tv_p", "p_rowsum")
+    am = B.run(Q, K, want=want_mx, mode=B.MODE_MXFP8, q_codes=qc, q_scales=qs, k_codes=kc, k_scales=ks,
+               region_bounds=rb)["_keepalive"][0]
+
+    lib, sp = B.load(), stream.cuda_stream
+
+    def mx_step():  # packs into the same code / scale buffers every call
+        B._check("kvprof_pack_mxfp8", lib.kvprof_pack_mxfp8(Q.data_ptr(), Q.numel() // 128, 128, sg.data_ptr(),
+                                                            qc.data_ptr(), qs.data_ptr(), sp))
+        B._check("kvprof_pack_mxfp8", lib.kvprof_pack_mxfp8(K.data_ptr(), K.numel() // 128, 128, sg.data_ptr(),
+                                                            kc.data_ptr(), ks.data_ptr(), sp))
+        B.kvprof_row_stats(am, stream)
+
+    ms_mx = time_it(mx_step, args.steps, args.warmup, stream)
+    rows = Q.shape[0] * Q.shape[1] * Q.shape[2]
+    return {"metric": METRIC, "value": round(rows / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "tiny three variants, 128 queries x 128 keys, all statistics and O",
+                       "variants": list(inputs.TINY_VARIANTS), "rows": rows},
+            "roofline": None, "us_per_call": round(ms * 1e3, 1),
+            "mxfp8": {"us_per_call": round(ms_mx * 1e3, 1), "note": "pack Q and K, then every statistic, TV, argmax and the P path"}}
+
+
 DECODE_BATCH = 512  # sequences per launch, seeds 5000 + b
 DECODE_BATCH_SEED0 = 5000
 
@@ -369,6 +415,8 @@ def main():
         out = run_decode(args)
     elif args.workload == "decode_batch":
         out = run_decode_batch(args)
+    elif args.workload == "tiny":
+        out = run_tiny(args)
     elif args.workload == "mx_sampled":
         out = run_mx(args)
     else:
