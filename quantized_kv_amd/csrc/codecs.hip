@@ -68,6 +68,82 @@ __global__ __launch_bounds__(64) void pack_mxfp8_kernel(const uint16_t* __restri
   }
 }
 
+// d = 128: eight lanes per row, sixteen consecutive elements per lane, eight rows per wave, so the
+// whole transform stays in registers. The butterfly runs in float64 (exact, as above): the four
+// stages inside a lane's sixteen elements first, then the three across the row's lanes (lane
+// bits 1, 2, 4 = element strides 16, 32, 64) by shuffles. A 32-element block is two lanes.
+__global__ __launch_bounds__(256) void pack_mxfp8_d128_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                              const int8_t* __restrict__ signs,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int sl = lane & 7;  // lane inside the row: elements 16 sl .. 16 sl + 15
+  const int64_t wave0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 8;
+  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6) * 8;
+  uint32_t sg[4] = {0u, 0u, 0u, 0u};
+  if (signs) {
+    const uint4 t = *reinterpret_cast<const uint4*>(signs + 16 * sl);
+    sg[0] = t.x; sg[1] = t.y; sg[2] = t.z; sg[3] = t.w;
+  }
+  for (int64_t r0 = wave0; r0 < rows; r0 += wstride) {  // wave-uniform loop: every lane shuffles
+    const int64_t r = r0 + (lane >> 3);
+    const bool ok = r < rows;
+    uint4 raw[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    if (ok) {
+      const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)r * 128 + 16 * sl);
+      raw[0] = src[0];
+      raw[1] = src[1];
+    }
+    double v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint4 q = raw[i >> 3];
+      const uint32_t w = (i & 6) == 0 ? q.x : (i & 6) == 2 ? q.y : (i & 6) == 4 ? q.z : q.w;
+      const double a = (double)bf16_to_f32((uint16_t)(w >> (16 * (i & 1))));
+      const bool neg = signs && ((sg[i >> 2] >> (8 * (i & 3))) & 0x80u);  // int8 -1 has its top bit set
+      v[i] = neg ? -a : a;
+    }
+    float y[16];
+    if (signs) {
+#pragma unroll
+      for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (!(i & h)) {
+            const double a0 = v[i], a1 = v[i + h];
+            v[i] = a0 + a1;
+            v[i + h] = a0 - a1;
+          }
+#pragma unroll
+      for (int b = 1; b < 8; b <<= 1) {
+        const bool hi = sl & b;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const double o = __shfl_xor(v[i], b);
+          v[i] = hi ? o - v[i] : v[i] + o;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = (float)__dmul_rn(v[i], kInvSqrt128);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = (float)v[i];
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(y[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    const int e = e8m0_exp(amax);
+    uint32_t cw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cw[i >> 2] |= (uint32_t)e4m3_rne(ldexpf(y[i], -e)) << (8 * (i & 3));
+    if (ok) {
+      *reinterpret_cast<uint4*>(codes + (size_t)r * 128 + 16 * sl) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+      if (!(sl & 1)) scales[(size_t)r * 4 + (sl >> 1)] = (uint8_t)(e + 127);
+    }
+  }
+}
+
 __global__ void unpack_mxfp8_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                     int64_t n, int d, float* __restrict__ out_f32,
                                     uint16_t* __restrict__ out_bf16) {
@@ -238,6 +314,12 @@ inline unsigned grid_for(int64_t n, int block, unsigned cap = 65536) {
 hipError_t launch_pack_mxfp8(const uint16_t* x, int64_t rows, int d, const int8_t* signs,
                              uint8_t* codes, uint8_t* scales, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  if (d == 128 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)codes & 15) == 0 && ((uintptr_t)signs & 15) == 0) {
+    const int64_t blocks = (rows + 31) / 32;  // 32 rows per 256-thread block
+    hipLaunchKernelGGL(pack_mxfp8_d128_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s,
+                       x, rows, signs, codes, scales);
+    return hipGetLastError();
+  }
   unsigned g = (unsigned)(rows < 65536 * 4 ? rows : 65536 * 4);
   hipLaunchKernelGGL(pack_mxfp8_kernel, dim3(g), dim3(64), 0, s, x, rows, d, signs, codes, scales);
   return hipGetLastError();

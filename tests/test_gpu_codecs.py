@@ -30,8 +30,8 @@ def test_pack_mxfp8_tiny_variants(kvprof_lib, rotate):
     assert np.array_equal(deq.astype(np.float64), O.mx_dequantize(oc, os_))
 
 
-@pytest.mark.parametrize("d", [32, 64, 256])
-def test_pack_mxfp8_other_widths_and_extremes(kvprof_lib, d):
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+def test_pack_mxfp8_widths_and_extremes(kvprof_lib, d):
     rng = np.random.default_rng(d)
     x = rng.standard_normal((37, d)).astype(np.float32) * 10.0 ** rng.integers(-30, 30, (37, 1))
     x[0] = 0.0  # all-zero block -> scale byte 0
@@ -47,6 +47,21 @@ def test_pack_mxfp8_other_widths_and_extremes(kvprof_lib, d):
         oc, os_ = O.pack_mxfp8(inputs.bf16_values(xb), sg)
         assert np.array_equal(_np(scales), os_)
         assert np.array_equal(_np(codes), oc)
+
+
+def test_pack_mxfp8_many_rows(kvprof_lib):
+    """More rows than one pass of the d = 128 kernel's grid covers (262,144 rows per pass): sampled
+    rows from the first pass, the second pass and the ragged end."""
+    rng = np.random.default_rng(7)
+    n = 262144 + 37
+    xb = inputs.to_bf16(rng.standard_normal((n, 128), dtype=np.float32))
+    signs = inputs.hadamard_signs(4)
+    codes, scales = B.kvprof_pack_mxfp8(xb.to(DEV), torch.from_numpy(signs).to(DEV))
+    torch.cuda.synchronize()
+    rows = np.r_[0:40, 131072:131080, 262136:n]
+    oc, os_ = O.pack_mxfp8(inputs.bf16_values(xb[rows]), signs)
+    assert np.array_equal(_np(scales)[rows], os_)
+    assert np.array_equal(_np(codes)[rows], oc)
 
 
 def test_pack_mxfp8_empty(kvprof_lib):
