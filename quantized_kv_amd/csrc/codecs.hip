@@ -181,6 +181,34 @@ __device__ __forceinline__ uint32_t int4_code(float x, Int4Meta mt) {
 }
 
 // K: one thread per (head, token group, channel pair).
+// The same decode, sixteen consecutive elements per thread (one 16-byte load of codes, one scale
+// byte: sixteen elements never straddle a 32-element block), written with 16-byte stores.
+__global__ void unpack_mxfp8_vec16_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                          int64_t n16, float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16) {
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n16; t += (int64_t)gridDim.x * blockDim.x) {
+    const uint4 c4 = reinterpret_cast<const uint4*>(codes)[t];
+    const int e = (int)scales[t >> 1] - 127;  // element 16 t lies in block (16 t) / 32
+    const uint32_t cw[4] = {c4.x, c4.y, c4.z, c4.w};
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = ldexpf(e4m3_value((uint8_t)(cw[i >> 2] >> (8 * (i & 3)))), e);
+    if (out_f32) {
+      float4* o = reinterpret_cast<float4*>(out_f32) + 4 * t;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+    if (out_bf16) {
+      uint32_t h[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        h[q] = (__float_as_uint(v[2 * q]) >> 16) | (__float_as_uint(v[2 * q + 1]) & 0xFFFF0000u);  // exact
+      uint4* o = reinterpret_cast<uint4*>(out_bf16) + 2 * t;
+      o[0] = make_uint4(h[0], h[1], h[2], h[3]);
+      o[1] = make_uint4(h[4], h[5], h[6], h[7]);
+    }
+  }
+}
+
 __global__ void pack_k_kernel(const uint16_t* __restrict__ k, int heads, int64_t N, int d, int R,
                               uint8_t* __restrict__ out, size_t blob) {
   Int4Layout L = int4_layout(N, d, R);
@@ -329,6 +357,12 @@ hipError_t launch_unpack_mxfp8(const uint8_t* codes, const uint8_t* scales, int6
                                float* out_f32, uint16_t* out_bf16, hipStream_t s) {
   int64_t n = rows * d;
   if (n == 0) return hipSuccess;
+  if (d % 32 == 0 && ((uintptr_t)codes & 15) == 0 && ((uintptr_t)out_f32 & 15) == 0 &&
+      ((uintptr_t)out_bf16 & 15) == 0) {
+    hipLaunchKernelGGL(unpack_mxfp8_vec16_kernel, dim3(grid_for(n / 16, 256)), dim3(256), 0, s, codes, scales,
+                       n / 16, out_f32, out_bf16);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(unpack_mxfp8_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, codes, scales, n,
                      d, out_f32, out_bf16);
   return hipGetLastError();

@@ -1297,7 +1297,9 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   }
 
   // ---- MXFP8 mode: bf16 reference row and the probability path ------------------------------------
-  if (MX) {
+  // None of these outputs depends on the exact ranks, so the main kernel writes them for every block,
+  // the redo blocks included, and the redo kernel (SLOW) leaves them alone.
+  if (MX && !SLOW) {
     __syncthreads();
     const RowInfo me = row_info(p, b, hkv, rb, r);
     const rsrc_t rkr = make_rsrc(p.k_ref + kvh * p.n_k * KVPROF_HEAD_DIM, head_bytes);

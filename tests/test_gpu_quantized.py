@@ -157,6 +157,46 @@ def test_mxfp8_video_sampled(kvprof_lib):
         _check_argmax(gv["argmax_ref"], ref["ref_scores"], "argmax_ref")
 
 
+def test_mxfp8_ties_and_redo(kvprof_lib):
+    """MXFP8 mode with the selection's hard cases (uniform rows, one dominant key, a block of 301
+    identical keys at the top-32 boundary): those row blocks go through the redo kernel, which
+    recomputes the ranks; the MX comparison outputs come from the main kernel."""
+    rng = np.random.default_rng(23)
+    Sk = 6240
+    k = rng.standard_normal((1, 1, Sk, 128)).astype(np.float32)
+    k[0, 0, 100:401] = k[0, 0, 7]
+    q = rng.standard_normal((1, 1, 16, 128)).astype(np.float32)
+    q[0, 0, 0:4] = 0.0
+    q[0, 0, 4:8] = k[0, 0, 5000] * 3.0
+    q[0, 0, 8:12] = k[0, 0, 7] * 0.4
+    Q, K = inputs.to_bf16(q), inputs.to_bf16(k)
+    signs = inputs.hadamard_signs(4)
+    sg = torch.from_numpy(signs).to(DEV)
+    qd, kd = Q.to(DEV), K.to(DEV)
+    qc, qs = B.kvprof_pack_mxfp8(qd.reshape(-1, 128), sg)
+    kc, ks = B.kvprof_pack_mxfp8(kd.reshape(-1, 128), sg)
+    bias = inputs.video_key_bias()
+    kw = dict(region_bounds=inputs.VIDEO_REGION_BOUNDS, frame_len=inputs.LF_TOKENS, n_frames=inputs.N_KEY_FRAMES)
+    want = ("support", "top_mass", "top32", "strict_zero", "region_mass", "frame_mass", "tv_qk", "argmax",
+            "argmax_ref", "p_zero_frac", "tv_p", "p_rowsum")
+    res = B.run(qd, kd, want=want, mode=B.MODE_MXFP8, q_codes=qc, q_scales=qs, k_codes=kc, k_scales=ks,
+                scale=128 ** -0.5, key_bias=torch.from_numpy(bias).to(DEV), **kw)
+    torch.cuda.synchronize()
+    # the workspace holds the decoded MX Q (16 x 128 bf16) and K (6240 x 128 bf16), then the redo list
+    ws = res["_keepalive"][1].cpu().numpy()
+    assert ws[4096 + Sk * 256:][:4].view(np.uint32)[0] == 1, "the row block was not redone"
+    g = _np(res)
+    ref = O.mx_row_stats(inputs.bf16_values(Q)[0, 0], inputs.bf16_values(K)[0, 0], signs, scale=128 ** -0.5,
+                         key_bias=bias, **kw)
+    P.check_rows(g, ref)
+    P.check_close("tv_qk", g["tv_qk"], ref["tv_qk"], atol=P.MASS_ATOL)
+    P.check_close("tv_p", g["tv_p"], ref["tv_p"], atol=P.MASS_ATOL)
+    P.check_close("p_rowsum", g["p_rowsum"], ref["p_rowsum"], atol=P.MASS_ATOL)
+    _check_zero_frac(g["p_zero_frac"], ref["p"], Sk)
+    _check_argmax(g["argmax"], ref["scores"], "argmax")
+    _check_argmax(g["argmax_ref"], ref["ref_scores"], "argmax_ref")
+
+
 def test_attend_int4_decode_batch(kvprof_lib):
     """Several sequences in one launch, one query position each (the decode step): batch b reads
     only its own packed KV heads."""
