@@ -301,6 +301,35 @@ __device__ __forceinline__ u32x4 load_k(const RowStatsParams& p, rsrc_t rk, cons
   }
 }
 
+// Int4 K of a key inside the 4-bit section, from its raw words (as load_k decodes them): the code
+// word of dims d0 .. d0+7 and their (scale, min) pairs.
+struct K4Raw {
+  uint32_t codes;
+  u32x4 m0, m1;
+};
+__device__ __forceinline__ K4Raw load_k4_raw(rsrc_t rk, const Int4Layout& L, int ja, int d0) {
+  K4Raw k;
+  k.codes = __builtin_amdgcn_raw_buffer_load_b32(rk, (unsigned)(L.kc + (size_t)ja * 64 + d0 / 2), 0, 0);
+  const unsigned mo = (unsigned)(L.km + ((size_t)(ja >> 5) * 128 + d0) * 4);
+  k.m0 = __builtin_amdgcn_raw_buffer_load_b128(rk, mo, 0, 0);
+  k.m1 = __builtin_amdgcn_raw_buffer_load_b128(rk, mo + 16u, 0, 0);
+  return k;
+}
+__device__ __forceinline__ u32x4 decode_k4(const K4Raw& k, u32x4& lo_out) {
+  f16x8 h, hl;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t wd = c < 4 ? k.m0[c] : k.m1[c - 4];
+    const float sc_ = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xFFFF));
+    const float mn_ = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
+    const float x = fmaf((float)((k.codes >> (4 * c)) & 0xF), sc_, mn_);
+    h[c] = (_Float16)x;
+    hl[c] = (_Float16)(x - (float)h[c]);
+  }
+  lo_out = __builtin_bit_cast(u32x4, hl);
+  return __builtin_bit_cast(u32x4, h);
+}
+
 // V values of key j, channels c0 .. c0+7 (c0 a multiple of 8), as f16 for the P.V product: one
 // 16-byte load for bf16; for int4 one word of codes and one of (scale, min), with the float32 window
 // selected branchlessly as in load_k. Keys past n_k read zeros.
@@ -515,6 +544,14 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
     for (int t = 0; t < kRing - 1 && t < TPW; ++t) issue(t);
   }
+  // Int4 keys of the 4-bit section: the raw words of the next tile are loaded while this one is
+  // decoded and multiplied (for row lengths up to 4,096 keys; longer rows have no registers left).
+  constexpr bool kPf4 = KSRC == KSRC_INT4 && TPW <= 32;
+  K4Raw pf4[4];
+  if (kPf4 && kbase + 16 <= (int)L.n) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pf4[ks] = load_k4_raw(rk, L, kbase + r, ks * 32 + 8 * g);
+  }
   // The scheduling barrier at the end of each tile keeps the compiler from hoisting every tile's
   // loads, which would push the score registers out to scratch.
 #pragma unroll
@@ -538,8 +575,17 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     } else {
       if (j0 < kmax) {
         u32x4 kf[4], kl[4];
+        if (kPf4 && j0 + 16 <= (int)L.n) {  // wave-uniform: this tile's raw words were loaded a tile ago
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kf[ks] = load_k<KSRC>(p, rk, L, j0 + r, ks * 32 + 8 * g, &kl[ks]);
+          for (int ks = 0; ks < 4; ++ks) kf[ks] = decode_k4(pf4[ks], kl[ks]);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) kf[ks] = load_k<KSRC>(p, rk, L, j0 + r, ks * 32 + 8 * g, &kl[ks]);
+        }
+        if (kPf4 && t + 1 < TPW && j0 + 32 <= (int)L.n) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) pf4[ks] = load_k4_raw(rk, L, j0 + 16 + r, ks * 32 + 8 * g);
+        }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           acc = mfma_step<KSRC>(kf[ks], sm.qs[r][ks * 4 + g], acc);
