@@ -489,3 +489,58 @@ def recall32(t_q: np.ndarray, t_ref: np.ndarray) -> float:
     a = set(int(x) for x in t_q if x >= 0)
     b = set(int(x) for x in t_ref if x >= 0)
     return len(a & b) / float(TOPK)
+
+
+# ----------------------------------------------------------------------------------------------
+# Local output ablation (P1, "当前判断与下一步优化空间 / Recommended sequence", first item: drop the
+# sink, the recent region or all history for the same sampled Q/K/V, renormalise P, and measure the
+# relative L2 and the cosine of the attention output before the output projection)
+# ----------------------------------------------------------------------------------------------
+
+def ablated_output(q, k, v, *, scale, key_bias=None, drop=(0, 0)):
+    """O_i = sum_j p'_ij v_j with p' the softmax over the keys outside the index range [lo, hi) only
+    (P renormalised over what is kept). Non-causal rows; at least one key must be kept."""
+    lo, hi = drop
+    sk = k.shape[0]
+    keep = np.ones(sk, dtype=bool)
+    keep[lo:hi] = False
+    if not keep.any():
+        raise ValueError("the ablation must keep at least one key")
+    kb = None if key_bias is None else np.asarray(key_bias, dtype=np.float64)[keep]
+    s = scores(q, np.asarray(k, dtype=np.float64)[keep], scale, key_bias=kb)
+    out = np.empty((s.shape[0], v.shape[1]), dtype=np.float64)
+    vk = np.asarray(v, dtype=np.float64)[keep]
+    for i in range(s.shape[0]):
+        out[i] = softmax_row(s[i]) @ vk
+    return out
+
+
+def cosine_rows(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Per-row cosine a_i.b_i / (|a_i| |b_i|); 0 where either row is the zero vector (reading: the page
+    gives no rule for a zero output)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    out = np.zeros(a.shape[0])
+    for i in range(a.shape[0]):
+        na, nb = np.linalg.norm(a[i]), np.linalg.norm(b[i])
+        if na > 0 and nb > 0:
+            out[i] = float(a[i] @ b[i]) / (na * nb)
+    return out
+
+
+def rel_l2_rows(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Per-row |a_i - b_i| / |b_i| (0 where b_i is the zero vector)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    num = np.linalg.norm(a - b, axis=1)
+    den = np.linalg.norm(b, axis=1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), 0.0)
+
+
+def ablation_metrics(o_abl: np.ndarray, o_full: np.ndarray) -> dict:
+    """Relative L2 and cosine of the ablated output against the full one: per row and over the whole
+    tensor (flattened), as P2 reports its output error per input tensor."""
+    fa = np.asarray(o_abl, dtype=np.float64).ravel()
+    ff = np.asarray(o_full, dtype=np.float64).ravel()
+    return {"rel_l2_row": rel_l2_rows(o_abl, o_full), "cos_row": cosine_rows(o_abl, o_full),
+            "rel_l2": rel_l2(fa, ff), "cos": float(fa @ ff) / (np.linalg.norm(fa) * np.linalg.norm(ff))}
