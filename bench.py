@@ -1,6 +1,6 @@
 """Benchmark of the KV-cache attention row profiler on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload sampled|full_rows|decode|decode_batch|mx_sampled|tiny] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload sampled|full_rows|decode|decode_batch|mx_sampled|ablation|tiny] [--no-cpu-baseline]
     python bench.py --copy-calibration     # 1 GiB device copy, for scaling the HBM byte counters
 
 A step is one kvprof_row_stats call over the whole workload with every statistic the workload
@@ -19,6 +19,9 @@ reports, inputs already resident in HBM:
 * mx_sampled: the sampled workload in MXFP8 mode: each step packs Q and K (signed-H128 + E4M3/E8M0
              K32) and computes every statistic on the MX rows plus TV / argmax against the bf16
              rows and the P path.
+* ablation : local output ablation over the sampled workload with V: O over all keys, then O with
+             the sink, the recent region and all history dropped (P renormalised over the kept keys),
+             each compared with the full O by per-row relative L2 and cosine.
 
 * tiny     : the three 128 x 128 variants (clean, early_focus, recent_focus) with every statistic and
              O in one call, and the same rows in MXFP8 mode (pack + statistics): launch-latency-bound,
@@ -47,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode", "decode_batch", "mx_sampled", "tiny"])
+    ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode", "decode_batch", "mx_sampled", "ablation", "tiny"])
     ap.add_argument("--records", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -398,6 +401,117 @@ def run_decode_batch(args):
             "input_gen_s": round(gen_s, 1)}
 
 
+ABLATION_DROPS = {"drop_sink": (0, 1560), "drop_recent": (1560, 3900), "drop_history": (0, 3900)}
+
+
+def cpu_baseline_ablation(n_records: int):
+    """The oracle, as it stands, on the ablation of the first n_records sampled records, one BLAS thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kvprof_oracle as O
+    from quantized_kv_amd import inputs
+
+    bias = inputs.video_key_bias().astype(np.float64)
+    dt, rows = 0.0, 0
+    for r in range(n_records):
+        rec = inputs.video_record(r, with_v=True, sampled=True)
+        q, k, v = inputs.bf16_values(rec.q), inputs.bf16_values(rec.k), inputs.bf16_values(rec.v)
+        with threadpool_limits(1):
+            t = time.perf_counter()
+            for h in range(q.shape[0]):
+                full = O.ablated_output(q[h], k[h], v[h], scale=128 ** -0.5, key_bias=bias)
+                for drop in ABLATION_DROPS.values():
+                    O.ablation_metrics(O.ablated_output(q[h], k[h], v[h], scale=128 ** -0.5, key_bias=bias,
+                                                        drop=drop), full)
+                rows += q.shape[1]
+            dt += time.perf_counter() - t
+    return {"value": round(rows / dt, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"records 0..{n_records - 1} of the ablation, {q.shape[0]} heads x {q.shape[1]} queries x "
+                      f"6240 keys, full + 3 ablations ({rows} rows, {dt:.1f} s of oracle time)"}
+
+
+def run_ablation(args):
+    """Local output ablation over the sampled workload (42 records x 32 heads x 96 queries x 6,240 keys
+    with V): one step = the full O, then for each of the three drops its key bias, O with P
+    renormalised over the kept keys (plus region masses, which show the dropped mass is 0), and the
+    per-row relative L2 and cosine against the full O."""
+    import torch
+
+    from quantized_kv_amd import binding as B
+    from quantized_kv_amd import inputs
+
+    dev = torch.device("cuda:0")
+    n_rec = args.records or inputs.N_RECORDS
+    t_gen = time.time()
+    qs, ks, vs = [], [], []
+    for r in range(n_rec):
+        rec = inputs.video_record(r, with_v=True, sampled=True)
+        qs.append(rec.q.to(dev))
+        ks.append(rec.k.to(dev))
+        vs.append(rec.v.to(dev))
+    Q, K, V = torch.stack(qs), torch.stack(ks), torch.stack(vs)
+    del qs, ks, vs
+    gen_s = time.time() - t_gen
+    Bn, H, Mq, _ = Q.shape
+    Sk = K.shape[2]
+    rows = Bn * H * Mq
+    bias = torch.from_numpy(inputs.video_key_bias()).to(dev)
+    kw = dict(scale=128 ** -0.5, region_bounds=inputs.VIDEO_REGION_BOUNDS)
+    want = ("o", "region_mass")
+    stream = torch.cuda.current_stream()
+    full = B.run(Q, K, V, want=want, attend=True, key_bias=bias, **kw)
+    biases = {n: B.kvprof_ablation_bias(Sk, d, key_bias=bias) for n, d in ABLATION_DROPS.items()}
+    runs = {n: B.run(Q, K, V, want=want, attend=True, key_bias=b, **kw) for n, b in biases.items()}
+    o_full = full["o"]
+    rel = torch.empty(rows, dtype=torch.float32, device=dev)
+    cos = torch.empty(rows, dtype=torch.float32, device=dev)
+    rsums = torch.empty(2 + 2 * rows, dtype=torch.float64, device=dev)
+    csums = torch.empty(3 + 3 * rows, dtype=torch.float64, device=dev)
+    lib = B.load()
+    sp = stream.cuda_stream
+
+    def step():
+        B.kvprof_attend(full["_keepalive"][0], stream)
+        for n, d in ABLATION_DROPS.items():
+            lib.kvprof_ablation_bias(bias.data_ptr(), Sk, d[0], d[1], biases[n].data_ptr(), sp)
+            B.kvprof_attend(runs[n]["_keepalive"][0], stream)
+            o = runs[n]["o"]
+            lib.kvprof_compare(o.data_ptr(), o_full.data_ptr(), None, None, rows, 128, rel.data_ptr(), None,
+                               rsums.data_ptr(), sp)
+            lib.kvprof_cosine(o.data_ptr(), o_full.data_ptr(), rows, 128, cos.data_ptr(), csums.data_ptr(), sp)
+
+    ms = time_it(step, args.steps, args.warmup, stream)
+    kern = lambda: B.kvprof_attend(runs["drop_sink"]["_keepalive"][0], stream)  # noqa: E731
+    ms_kernel = time_it(kern, args.steps, 1, stream)
+    # one attend launch: K and V once per (record, head), Q, the bias, O and the region masses
+    nbytes = K.numel() * 2 + V.numel() * 2 + Q.numel() * 2 + Sk * 4 + rows * (128 * 4 + 3 * 4)
+    gbs = nbytes / (ms_kernel * 1e-3) / 1e9
+    summary = {}
+    for n in ABLATION_DROPS:
+        o = runs[n]["o"]
+        B.kvprof_compare(o, o_full)  # warm, unchecked
+        r_row, _, rs = B.kvprof_compare(o, o_full)
+        c_row, cs = B.kvprof_cosine(o, o_full)
+        torch.cuda.synchronize()
+        rs, cs = rs.cpu().tolist(), cs.cpu().tolist()
+        summary[n] = {"rel_l2": round((rs[0] / rs[1]) ** 0.5, 5), "cos": round(cs[0] / (cs[1] * cs[2]) ** 0.5, 5),
+                      "rel_l2_row_median": round(float(r_row.median()), 5),
+                      "cos_row_median": round(float(c_row.median()), 5)}
+    out = {"metric": METRIC, "value": round(rows / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "local output ablation, video steady chunk, sampled queries", "records": Bn,
+                      "heads": H, "queries_per_head": Mq, "keys": Sk, "head_dim": 128, "rows_per_step": rows,
+                      "ablations": list(ABLATION_DROPS)},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes},
+           "attend_kernel_ms": round(ms_kernel, 4), "ablation": summary, "input_gen_s": round(gen_s, 1)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_ablation(3)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -419,6 +533,8 @@ def main():
         out = run_tiny(args)
     elif args.workload == "mx_sampled":
         out = run_mx(args)
+    elif args.workload == "ablation":
+        out = run_ablation(args)
     else:
         out = run_video(args, sampled=args.workload == "sampled")
     print(json.dumps(out), flush=True)

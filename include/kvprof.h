@@ -195,6 +195,29 @@ int kvprof_compare(const float* o_q, const float* o_ref, const int32_t* top32_q,
                    const int32_t* top32_ref, int64_t rows, int32_t d, float* rel_l2_row,
                    float* recall_row, double* sums, void* stream);
 
+/* Local output ablation ("Catnip Week 10 KV Cache Attention Study", section on the current judgement
+ * and next steps, recommended sequence, first item: drop the sink, the recent region or all history,
+ * renormalise P, compare the output by relative L2 and cosine).
+ *
+ * kvprof_ablation_bias writes the key bias that drops keys [drop_lo, drop_hi):
+ *   out[j] = key_bias[j] (0 when key_bias is NULL), plus -1e4 for drop_lo <= j < drop_hi.
+ * A row_stats/attend call with this bias gives every dropped key an exponential that is exactly 0 in
+ * float32, so its O is the output with P renormalised over the kept keys. Rows must see at least one
+ * kept key (non-causal rows always do, since the range may not cover every key).
+ *   key_bias  device float32 [n_k] or NULL;  out  device float32 [n_k] (may equal key_bias)
+ * Errors: EINVAL (n_k < 1, null out, range outside [0, n_k], range covering every key), EALIGN.
+ *
+ * kvprof_cosine: cos_row[i] = a_i.b_i / (|a_i| |b_i|) (0 if either row is zero), float64 accumulation;
+ *   a, b      device float32 [rows][d]; cos_row  device float32 [rows]
+ *   sums      device double [3 + 3*rows]: sums[0] = sum_i a_i.b_i, sums[1] = sum_i |a_i|^2,
+ *             sums[2] = sum_i |b_i|^2 (tensor-level cosine = sums[0] / sqrt(sums[1] sums[2])); the
+ *             remaining 3*rows entries are scratch. Sums run in row order (deterministic).
+ * Errors: EINVAL (rows < 0, d < 1, null pointers), EALIGN (sums not 8-byte aligned). */
+int kvprof_ablation_bias(const float* key_bias, int32_t n_k, int32_t drop_lo, int32_t drop_hi, float* out,
+                         void* stream);
+int kvprof_cosine(const float* a, const float* b, int64_t rows, int32_t d, float* cos_row, double* sums,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

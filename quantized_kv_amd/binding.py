@@ -88,8 +88,11 @@ def load(path: str = LIB_PATH):
     lib.kvprof_row_stats.argtypes = [ctypes.POINTER(KvprofArgs), _P]
     lib.kvprof_attend.argtypes = [ctypes.POINTER(KvprofArgs), _P]
     lib.kvprof_compare.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]
+    lib.kvprof_ablation_bias.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
+    lib.kvprof_cosine.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]
     for name in ("kvprof_pack_mxfp8", "kvprof_unpack_mxfp8", "kvprof_pack_int4kv",
-                 "kvprof_unpack_int4kv", "kvprof_row_stats", "kvprof_attend", "kvprof_compare"):
+                 "kvprof_unpack_int4kv", "kvprof_row_stats", "kvprof_attend", "kvprof_compare",
+                 "kvprof_ablation_bias", "kvprof_cosine"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -252,6 +255,28 @@ def kvprof_compare(o_q, o_ref, top32_q=None, top32_ref=None, stream=None):
     _check("kvprof_compare", load().kvprof_compare(_ptr(o_q), _ptr(o_ref), _ptr(top32_q), _ptr(top32_ref), rows, d,
                                                    _ptr(rel), _ptr(rec), _ptr(sums), _stream(stream)))
     return rel, rec, sums[:2]
+
+
+def kvprof_ablation_bias(n_k: int, drop, key_bias=None, device=None, stream=None):
+    """Key bias that drops keys [lo, hi) (local output ablation); returns a float32 [n_k] tensor."""
+    import torch
+
+    dev = key_bias.device if key_bias is not None else device
+    out = torch.empty(n_k, dtype=torch.float32, device=dev)
+    _check("kvprof_ablation_bias", load().kvprof_ablation_bias(_ptr(key_bias), n_k, int(drop[0]), int(drop[1]),
+                                                               _ptr(out), _stream(stream)))
+    return out
+
+
+def kvprof_cosine(a, b, stream=None):
+    """Per-row cosine of two float32 [rows, d] tensors, plus the three sums of the tensor-level cosine."""
+    import torch
+
+    rows, d = a.shape
+    cos = torch.empty(rows, dtype=torch.float32, device=a.device)
+    sums = torch.empty(3 + 3 * rows, dtype=torch.float64, device=a.device)
+    _check("kvprof_cosine", load().kvprof_cosine(_ptr(a), _ptr(b), rows, d, _ptr(cos), _ptr(sums), _stream(stream)))
+    return cos, sums[:3]
 
 
 def run(q, k=None, v=None, *, want=("support", "top_mass", "top32", "strict_zero", "row_max", "row_lse"),

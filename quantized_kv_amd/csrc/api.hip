@@ -10,6 +10,12 @@
 
 #include "kvprof_internal.h"
 
+namespace kvp {  // ablation.hip
+hipError_t launch_ablation_bias(const float* bias, int n_k, int lo, int hi, float* out, hipStream_t s);
+hipError_t launch_cosine(const float* a, const float* b, int64_t rows, int d, float* cos_row, double* sums,
+                         hipStream_t s);
+}  // namespace kvp
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -373,6 +379,28 @@ int kvprof_compare(const float* o_q, const float* o_ref, const int32_t* top32_q,
   return launched(kvp::launch_compare(o_q, o_ref, top32_q, top32_ref, rows, d, rel_l2_row, recall_row, sums,
                                       reinterpret_cast<hipStream_t>(stream)),
                   "compare");
+}
+
+int kvprof_ablation_bias(const float* key_bias, int32_t n_k, int32_t drop_lo, int32_t drop_hi, float* out,
+                         void* stream) {
+  if (n_k < 1) return fail(KVPROF_EINVAL, "n_k must be >= 1 (got %d)", n_k);
+  if (!out) return fail(KVPROF_EINVAL, "null output");
+  if (drop_lo < 0 || drop_hi < drop_lo || drop_hi > n_k)
+    return fail(KVPROF_EINVAL, "drop range [%d, %d) must lie in [0, %d]", drop_lo, drop_hi, n_k);
+  if (drop_hi - drop_lo == n_k) return fail(KVPROF_EINVAL, "the ablation must keep at least one key");
+  if (!aligned(out, 4) || (key_bias && !aligned(key_bias, 4))) return fail(KVPROF_EALIGN, "float arrays must be 4-byte aligned");
+  return launched(kvp::launch_ablation_bias(key_bias, n_k, drop_lo, drop_hi, out,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                  "ablation_bias");
+}
+
+int kvprof_cosine(const float* a, const float* b, int64_t rows, int32_t d, float* cos_row, double* sums,
+                  void* stream) {
+  if (rows < 0 || d < 1) return fail(KVPROF_EINVAL, "rows must be >= 0 and d >= 1");
+  if (rows > 0 && (!a || !b || !cos_row || !sums)) return fail(KVPROF_EINVAL, "null pointer");
+  if (sums && !aligned(sums, 8)) return fail(KVPROF_EALIGN, "sums must be 8-byte aligned");
+  return launched(kvp::launch_cosine(a, b, rows, d, cos_row, sums, reinterpret_cast<hipStream_t>(stream)),
+                  "cosine");
 }
 
 }  // extern "C"

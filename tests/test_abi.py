@@ -20,7 +20,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = B.declared_functions()
     assert {"kvprof_pack_mxfp8", "kvprof_pack_int4kv", "kvprof_row_stats", "kvprof_attend",
-            "kvprof_int4kv_bytes", "kvprof_compare", "kvprof_workspace_bytes"} <= set(names)
+            "kvprof_int4kv_bytes", "kvprof_compare", "kvprof_workspace_bytes", "kvprof_ablation_bias",
+            "kvprof_cosine"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert lib.kvprof_abi_version() == 1
@@ -121,3 +122,20 @@ def test_region_and_workspace_validation(lib):
     a = _args()
     assert lib.kvprof_attend(ctypes.byref(a), None) == B.KVPROF_EINVAL  # attend needs o
     assert lib.kvprof_compare(None, None, None, None, 4, 128, None, None, None, None) == B.KVPROF_EINVAL
+
+
+def test_ablation_entry_points_validate(lib):
+    """Local output ablation entry points reject bad ranges and pointers before any launch."""
+    fake = ctypes.c_void_p(256)  # never dereferenced: every call below fails validation
+    assert lib.kvprof_ablation_bias(None, 0, 0, 0, fake, None) == B.KVPROF_EINVAL
+    assert lib.kvprof_ablation_bias(None, 100, 0, 0, None, None) == B.KVPROF_EINVAL
+    assert lib.kvprof_ablation_bias(None, 100, 5, 4, fake, None) == B.KVPROF_EINVAL
+    assert lib.kvprof_ablation_bias(None, 100, -1, 4, fake, None) == B.KVPROF_EINVAL
+    assert lib.kvprof_ablation_bias(None, 100, 0, 101, fake, None) == B.KVPROF_EINVAL
+    assert lib.kvprof_ablation_bias(None, 100, 0, 100, fake, None) == B.KVPROF_EINVAL
+    assert b"keep at least one key" in lib.kvprof_last_error()
+    assert lib.kvprof_ablation_bias(None, 100, 0, 10, ctypes.c_void_p(258), None) == B.KVPROF_EALIGN
+    assert lib.kvprof_cosine(None, None, -1, 128, None, None, None) == B.KVPROF_EINVAL
+    assert lib.kvprof_cosine(None, None, 4, 0, None, None, None) == B.KVPROF_EINVAL
+    assert lib.kvprof_cosine(None, fake, 4, 128, fake, fake, None) == B.KVPROF_EINVAL
+    assert lib.kvprof_cosine(fake, fake, 4, 128, fake, ctypes.c_void_p(260), None) == B.KVPROF_EALIGN

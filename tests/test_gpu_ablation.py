@@ -1,0 +1,105 @@
+"""GPU parity of the local output ablation (drop the sink, the recent region or all history, P
+renormalised over the kept keys; relative L2 and cosine of O) against the oracle, through the C ABI.
+
+The full video record runs on the GPU (32 heads x 96 sampled queries x 6,240 keys); the oracle computes
+three heads. Tolerances: O per row 1e-3 relative (as for every O); the per-row relative L2 and cosine
+are taken from two outputs that each carry that error, so they may differ from the oracle's by
+2e-3 (1 + value) at most; the cosine kernel itself is compared with the oracle's cosine of the same
+float32 outputs to 1e-6."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvprof_oracle as O
+from quantized_kv_amd import binding as B
+from quantized_kv_amd import inputs
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+DROPS = {"drop_sink": (0, 1560), "drop_recent": (1560, 3900), "drop_history": (0, 3900)}
+METRIC_TOL = 2e-3
+
+
+def test_ablation_bias_values(kvprof_lib):
+    bias = inputs.video_key_bias()
+    bt = torch.from_numpy(bias).to(DEV)
+    for lo, hi in list(DROPS.values()) + [(0, 0), (6239, 6240), (1, 6240)]:
+        out = B.kvprof_ablation_bias(6240, (lo, hi), key_bias=bt).cpu().numpy()
+        exp = bias.astype(np.float32).copy()
+        exp[lo:hi] = exp[lo:hi] + np.float32(-1.0e4)
+        assert np.array_equal(out, exp)
+    out = B.kvprof_ablation_bias(37, (3, 9), device=DEV).cpu().numpy()
+    exp = np.zeros(37, np.float32)
+    exp[3:9] = -1.0e4
+    assert np.array_equal(out, exp)
+
+
+@pytest.mark.parametrize("rows", [0, 1, 1000, 4099])
+def test_cosine_kernel(kvprof_lib, rows):
+    rng = np.random.default_rng(rows)
+    a = rng.standard_normal((rows, 128)).astype(np.float32)
+    b = (a + 0.3 * rng.standard_normal((rows, 128))).astype(np.float32)
+    if rows > 3:
+        a[1] = 0.0
+        b[2] = -2.0 * a[2]
+    cos, sums = B.kvprof_cosine(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV))
+    torch.cuda.synchronize()
+    if rows == 0:
+        return
+    ref = O.cosine_rows(a, b)
+    assert np.abs(cos.cpu().numpy() - ref).max() <= 1e-6
+    s = sums.cpu().numpy()
+    a64, b64 = a.astype(np.float64), b.astype(np.float64)
+    assert s[0] == pytest.approx((a64 * b64).sum(), rel=1e-12)
+    assert s[1] == pytest.approx((a64 * a64).sum(), rel=1e-12)
+    assert s[2] == pytest.approx((b64 * b64).sum(), rel=1e-12)
+    m = O.ablation_metrics(a, b)
+    assert s[0] / np.sqrt(s[1] * s[2]) == pytest.approx(m["cos"], abs=1e-12)
+
+
+def test_local_output_ablation_video_record(kvprof_lib):
+    rec = inputs.video_record(0, with_v=True, sampled=True)
+    bias = inputs.video_key_bias()
+    bt = torch.from_numpy(bias).to(DEV)
+    q, k, v = rec.q[None].to(DEV), rec.k[None].to(DEV), rec.v[None].to(DEV)
+    kw = dict(scale=128 ** -0.5, region_bounds=inputs.VIDEO_REGION_BOUNDS)
+    full = B.run(q, k, v, want=("o", "region_mass"), attend=True, key_bias=bt, **kw)
+    o_full = full["o"]
+    qv, kv, vv = inputs.bf16_values(rec.q), inputs.bf16_values(rec.k), inputs.bf16_values(rec.v)
+    heads = (0, 17, 31)
+    Mq = rec.q.shape[1]
+    ref_full = {h: O.ablated_output(qv[h], kv[h], vv[h], scale=128 ** -0.5, key_bias=bias) for h in heads}
+    of = o_full.cpu().numpy().reshape(32, Mq, 128)
+    for h in heads:
+        P.check_o(of[h], ref_full[h])
+    for name, (lo, hi) in DROPS.items():
+        ab = B.kvprof_ablation_bias(6240, (lo, hi), key_bias=bt)
+        g = B.run(q, k, v, want=("o", "region_mass"), attend=True, key_bias=ab, **kw)
+        rel, _, rsums = B.kvprof_compare(g["o"], o_full)
+        cos, csums = B.kvprof_cosine(g["o"], o_full)
+        torch.cuda.synchronize()
+        go = g["o"].cpu().numpy().reshape(32, Mq, 128)
+        # the dropped regions carry no mass in any row (a property at full size)
+        rm = g["region_mass"].cpu().numpy()
+        for r, (a, b) in enumerate(zip(inputs.VIDEO_REGION_BOUNDS[:-1], inputs.VIDEO_REGION_BOUNDS[1:])):
+            if lo <= a and b <= hi:
+                assert np.all(rm[:, r] == 0.0), (name, r)
+        assert np.allclose(rm.sum(axis=1), 1.0, atol=2e-3)
+        relg = rel.cpu().numpy().reshape(32, Mq)
+        cosg = cos.cpu().numpy().reshape(32, Mq)
+        for h in heads:
+            ref = O.ablated_output(qv[h], kv[h], vv[h], scale=128 ** -0.5, key_bias=bias, drop=(lo, hi))
+            P.check_o(go[h], ref)
+            m = O.ablation_metrics(ref, ref_full[h])
+            assert np.all(np.abs(relg[h] - m["rel_l2_row"]) <= METRIC_TOL * (1 + m["rel_l2_row"])), name
+            assert np.all(np.abs(cosg[h] - m["cos_row"]) <= METRIC_TOL * (1 + np.abs(m["cos_row"]))), name
+        # tensor-level figures from the device sums, against the oracle over the same three heads'
+        # GPU outputs (exact fp64 identities) and overall consistency with the per-row values
+        rs, cs = rsums.cpu().numpy(), csums.cpu().numpy()
+        tensor_rel = np.sqrt(rs[0] / rs[1])
+        tensor_cos = cs[0] / np.sqrt(cs[1] * cs[2])
+        mg = O.ablation_metrics(go.reshape(-1, 128), of.reshape(-1, 128))
+        assert tensor_rel == pytest.approx(mg["rel_l2"], rel=1e-9)
+        assert tensor_cos == pytest.approx(mg["cos"], abs=1e-9)
+        assert 0.0 < tensor_rel and -1.0 <= tensor_cos <= 1.0
