@@ -875,7 +875,10 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   }
   __syncthreads();
   const bool slow_path = sm.flag != 0;
-  if (!SLOW && slow_path && tid == 0) {  // left to the redo kernel, which rewrites every output
+  // Only the top-32 list, the top-f masses and the MX argmax depend on the ranks. Without them a
+  // slow-path block needs no redo: it skips the gather, and phase E writes none of those outputs.
+  const bool need_ranks = p.top32 != nullptr || p.top_mass != nullptr || (MX && p.argmax != nullptr);
+  if (!SLOW && slow_path && need_ranks && tid == 0) {  // left to the redo kernel, which rewrites every output
     const unsigned k = atomicAdd(p.redo, 1u);
     p.redo[1 + k] = (unsigned)bid;
   }

@@ -103,3 +103,28 @@ def test_local_output_ablation_video_record(kvprof_lib):
         assert tensor_rel == pytest.approx(mg["rel_l2"], rel=1e-9)
         assert tensor_cos == pytest.approx(mg["cos"], abs=1e-9)
         assert 0.0 < tensor_rel and -1.0 <= tensor_cos <= 1.0
+
+
+def test_hard_rows_without_rank_outputs(kvprof_lib):
+    """Rows whose selection needs the slow path (uniform rows, one dominant key, a block of 301 equal
+    keys) with no rank-dependent output requested: no redo runs, and every other output still matches."""
+    rng = np.random.default_rng(17)
+    Sk = 6240
+    k = rng.standard_normal((1, 1, Sk, 128)).astype(np.float32)
+    k[0, 0, 100:401] = k[0, 0, 7]
+    q = rng.standard_normal((1, 1, 16, 128)).astype(np.float32)
+    q[0, 0, 0:4] = 0.0
+    q[0, 0, 4:8] = k[0, 0, 5000] * 3.0
+    q[0, 0, 8:12] = k[0, 0, 7] * 0.4
+    v = rng.standard_normal((1, 1, Sk, 128)).astype(np.float32)
+    Q, K, V = inputs.to_bf16(q), inputs.to_bf16(k), inputs.to_bf16(v)
+    bias = inputs.video_key_bias()
+    kw = dict(region_bounds=inputs.VIDEO_REGION_BOUNDS, frame_len=inputs.LF_TOKENS, n_frames=inputs.N_KEY_FRAMES)
+    want = ("support", "strict_zero", "row_max", "row_lse", "region_mass", "frame_mass", "o")
+    g = B.run(Q.to(DEV), K.to(DEV), V.to(DEV), want=want, attend=True, scale=128 ** -0.5,
+              key_bias=torch.from_numpy(bias).to(DEV), **kw)
+    torch.cuda.synchronize()
+    gn = {n: g[n].cpu().numpy() for n in want}
+    ref = O.row_stats(inputs.bf16_values(Q)[0, 0], inputs.bf16_values(K)[0, 0], scale=128 ** -0.5,
+                      key_bias=bias, v=inputs.bf16_values(V)[0, 0], **kw)
+    P.check_rows(gn, ref)
