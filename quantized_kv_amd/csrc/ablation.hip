@@ -52,14 +52,13 @@ __global__ __launch_bounds__(64) void cosine_kernel(const float* __restrict__ a,
   }
 }
 
-// Fixed-order sums of the partials: 256 contiguous chunks, then the chunk sums in order.
+// Fixed-order sums of the partials: 256 interleaved subsets, then the subset sums in order.
 __global__ __launch_bounds__(256) void cosine_sum_kernel(const double* __restrict__ part, long long rows,
                                                          double* __restrict__ sums) {
   __shared__ double s[3][256];
   const int t = threadIdx.x;
-  const long long per = (rows + 255) / 256;
   double x = 0.0, y = 0.0, z = 0.0;
-  for (long long i = t * per; i < (t + 1) * per && i < rows; ++i) {
+  for (long long i = t; i < rows; i += 256) {  // thread t sums rows t, t + 256, ... (coalesced)
     x += part[3 * i];
     y += part[3 * i + 1];
     z += part[3 * i + 2];

@@ -120,9 +120,8 @@ __global__ __launch_bounds__(256) void compare_sum_kernel(const double* __restri
                                                           double* __restrict__ sums) {
   __shared__ double sd[256], sn[256];
   const int t = threadIdx.x;
-  long long per = (rows + 255) / 256;
   double a = 0.0, b = 0.0;
-  for (long long i = t * per; i < (t + 1) * per && i < rows; ++i) {
+  for (long long i = t; i < rows; i += 256) {  // thread t sums rows t, t + 256, ... (coalesced)
     a += part[2 * i];
     b += part[2 * i + 1];
   }

@@ -882,7 +882,8 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     const unsigned k = atomicAdd(p.redo, 1u);
     p.redo[1 + k] = (unsigned)bid;
   }
-  if (!slow_path) {
+  if (!slow_path && need_ranks) {  // (without rank outputs the gather is skipped: phase E reads its
+                                    // results only for the top-32 list, the top-f masses and the argmax)
     {
       // boundary bins of this lane's row (level-1 bins; keys below the threshold get bin 256). The
       // list holds every key of a bin <= bq0 (the top-32 boundary bin and the bins above it: at most
@@ -1006,7 +1007,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       }
     }
     __syncthreads();
-  } else if (SLOW) {
+  } else if (SLOW && need_ranks) {  // here slow_path holds
   // ---- D: refine and gather, one target at a time --------------------------------------------------
 #pragma unroll 1
   for (int t = 0; t < NT; ++t) {
