@@ -58,6 +58,7 @@ __global__ __launch_bounds__(256) void cosine_sum_kernel(const double* __restric
   __shared__ double s[3][256];
   const int t = threadIdx.x;
   double x = 0.0, y = 0.0, z = 0.0;
+#pragma unroll 8  // loads issued ahead; the additions keep their order
   for (long long i = t; i < rows; i += 256) {  // thread t sums rows t, t + 256, ... (coalesced)
     x += part[3 * i];
     y += part[3 * i + 1];

@@ -121,6 +121,7 @@ __global__ __launch_bounds__(256) void compare_sum_kernel(const double* __restri
   __shared__ double sd[256], sn[256];
   const int t = threadIdx.x;
   double a = 0.0, b = 0.0;
+#pragma unroll 8  // loads issued ahead; the additions keep their order
   for (long long i = t; i < rows; i += 256) {  // thread t sums rows t, t + 256, ... (coalesced)
     a += part[2 * i];
     b += part[2 * i + 1];
