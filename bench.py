@@ -107,8 +107,9 @@ def time_it(fn, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps  # ms per call
 
 
-def cpu_baseline_video(n_records: int, sampled: bool):
-    """The oracle, as it stands, on the first n_records records (all heads), one BLAS thread."""
+def cpu_baseline_video(n_records: int, sampled: bool, threads=1):
+    """The oracle, as it stands, on the first n_records records (all heads), with `threads` BLAS
+    threads (None: every core of the host)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -120,7 +121,7 @@ def cpu_baseline_video(n_records: int, sampled: bool):
     for r in range(n_records):
         rec = inputs.video_record(r, with_v=False, sampled=sampled)
         q, k = inputs.bf16_values(rec.q), inputs.bf16_values(rec.k)
-        with threadpool_limits(1):
+        with threadpool_limits(threads):
             t = time.perf_counter()
             for h in range(q.shape[0]):
                 O.row_stats(q[h], k[h], scale=128 ** -0.5, key_bias=bias,
@@ -128,7 +129,13 @@ def cpu_baseline_video(n_records: int, sampled: bool):
                             n_frames=inputs.N_KEY_FRAMES)
                 rows += q.shape[1]
             dt += time.perf_counter() - t
-    return {"value": round(rows / dt, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+    if threads is None:  # the BLAS thread count in effect (OMP / OpenBLAS settings of the host)
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    else:
+        cores = threads
+    return {"value": round(rows / dt, 1), "unit": "rows/s", "cores": cores, "kind": "oracle",
             "sample": f"records 0..{n_records - 1}, {q.shape[0]} heads x {q.shape[1]} queries x 6240 keys "
                       f"({rows} rows, {dt:.1f} s of oracle time)"}
 
@@ -203,6 +210,8 @@ def run_video(args, sampled: bool):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_video(6 if sampled else 1, sampled)
+        # the same oracle with NumPy's BLAS on every host core (its per-row loops stay single-threaded)
+        out["cpu_baseline_all_cores"] = cpu_baseline_video(3 if sampled else 1, sampled, threads=None)
     return out
 
 
