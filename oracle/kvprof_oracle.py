@@ -150,13 +150,7 @@ def row_stats(q, k, *, scale, key_bias=None, causal=False, q_pos0=0, region_boun
         p = softmax_row(s[i])
         out["p"].append(p)
         out["support"].append(entropy_support(p[:ni], ni))
-        # one sort per row serves the three top-f masses (same definition as top_mass)
-        ps = p[:ni][sorted_desc(p[:ni])]
-        tm = []
-        for pct in TOP_PCTS:
-            kf, rem = divmod(ni * pct, 100)
-            tm.append(float(np.sum(ps[:kf])) + ((rem / 100.0) * float(ps[kf]) if kf < ni else 0.0))
-        out["top_mass"].append(tm)
+        out["top_mass"].append([top_mass(p, ni, pct) for pct in TOP_PCTS])
         out["top32"].append(top32(s[i], ni))
         out["strict_zero"].append(strict_zero_count(s[i], ni))
         if region_bounds is not None:
