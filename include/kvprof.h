@@ -26,6 +26,14 @@
  *   - The library never allocates device memory. Scratch space comes from the caller's workspace
  *     (kvprof_workspace_bytes). Outputs must not alias inputs.
  *   - Results are bitwise deterministic for identical inputs and launch configuration.
+ *   - Element types: the pages take Q/K/V at the bf16 production boundary ("Catnip Week 10 KV Cache
+ *     Attention Study", experiment design: BF16 boundary tensors against an FP32 reference), so every
+ *     tensor input is bf16 and rows are dense (row stride = d). The codec calls therefore carry no
+ *     dtype or leading-dimension argument; a strided or float32 source is copied to dense bf16 by the
+ *     caller first.
+ *   - Range: the P.V product and the INT4KV scores run on f16 MFMAs. V (every call that writes o) and,
+ *     in INT4KV mode, Q must lie within the f16 range (|x| < 65520); larger values overflow to inf.
+ *     bf16 values below 2^-14 in magnitude lose mantissa bits there (f16 subnormals).
  */
 #ifndef KVPROF_H
 #define KVPROF_H
@@ -72,7 +80,7 @@ const char* kvprof_last_error(void);
  *   signs   device int8 [d] of +1/-1, or NULL for no rotation. With signs, d must be a power of two
  *           in [32, 256]; the rotation is y = (signs * x) H_d / sqrt(d) with exact float64 sums, the
  *           product with the float64 constant 1/sqrt(d) rounded to float64 and then to float32.
- *   d       multiple of 32.
+ *   d       multiple of 32, at most 256.
  *   codes   uint8 [rows][d] E4M3FN codes (round to nearest even, -0 kept as 0x80).
  *   scales  uint8 [rows][d/32] E8M0 bytes e+127, e = the smallest integer with amax <= 448 * 2^e,
  *           clamped to [-127, 127] (amax = 0 gives -127); no element saturates.
@@ -82,7 +90,8 @@ int kvprof_pack_mxfp8(const uint16_t* x, int64_t rows, int32_t d, const int8_t* 
                       uint8_t* codes, uint8_t* scales, void* stream);
 
 /* Decode MXFP8 rows: out[r][c] = E4M3(codes[r][c]) * 2^(scales[r][c/32] - 127) as float32.
- * Errors as for kvprof_pack_mxfp8. */
+ * ("Catnip Week 10 KV Cache Attention Study": experiment design step 4, E4M3 elements with E8M0 K32
+ *  scales.) d: a multiple of 32 up to 256. Errors as for kvprof_pack_mxfp8. */
 int kvprof_unpack_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t d,
                         float* out, void* stream);
 
@@ -164,6 +173,8 @@ typedef struct kvprof_args {
 } kvprof_args;
 
 /* Workspace bytes kvprof_row_stats / kvprof_attend need for these arguments (0 for invalid ones).
+ * (The pages reduce on the GPU and move only small arrays off it — "Catnip Week 10 KV Cache Attention
+ *  Study", experiment design, GPU-side reduction — so intermediate state stays in this device buffer.)
  * Every call with at least one row needs some: a list of the 16-row blocks whose exact ranks take
  * the slow path (4 bytes per block + 4), plus the decoded MXFP8 operands and, for heatmaps or
  * histograms requested without their per-row inputs, those per-row arrays. The contents need no
@@ -171,12 +182,19 @@ typedef struct kvprof_args {
 size_t kvprof_workspace_bytes(const kvprof_args* a);
 
 /* Row statistics over bf16 or MXFP8 scores (modes BF16 and MXFP8), optionally with O = P.V.
+ * ("Catnip Week 10 KV Cache Attention Study": the Structural / Effective / Numerical MXFP8 definitions
+ *  of the experiment design — strict zeros, exp(H)/Sk support, top-1/5/10 % mass, region masses of the
+ *  KV-cache banner, Figure 2's key-frame masses, Figure 5's histograms; the section on Q/K and
+ *  probability quantization for TV, argmax agreement and the P-path. Top-32 indices: the MiniCPM5-2B
+ *  predictor study, section 0.)
  * Requires d == 128 and n_k <= KVPROF_MAX_KEYS (KVPROF_MAX_KEYS_MX in MXFP8 mode).
  * Errors: EINVAL, ESHAPE, EALIGN (q, k, v, codes not 16-byte aligned), ESIZE (workspace),
  * EUNSUPPORTED (n_k or region/frame counts beyond the limits), ELAUNCH. */
 int kvprof_row_stats(const kvprof_args* a, void* stream);
 
-/* Attention output O = softmax(scale q k^T + bias, causal) V over bf16 K/V (mode BF16) or over packed
+/* ("KV residual window": the output of attention over the dequantized cache and its relative L2; the
+ *  MiniCPM5-2B predictor study, section 0: the GQA decode shape and recall@32.)
+ * Attention output O = softmax(scale q k^T + bias, causal) V over bf16 K/V (mode BF16) or over packed
  * 4-bit K/V with the float32 recent window (mode INT4KV), with any of the row statistics (the top-32
  * indices and region masses give recall@32 and the recent-window mass). o is required. */
 int kvprof_attend(const kvprof_args* a, void* stream);
@@ -189,7 +207,9 @@ int kvprof_attend(const kvprof_args* a, void* stream);
  *   sums           device double [2 + 2*rows]: sums[0] = sum_i ||o_q[i] - o_ref[i]||^2 and
  *                  sums[1] = sum_i ||o_ref[i]||^2 (the square root of their ratio is the tensor-level
  *                  relative L2); the remaining 2*rows entries are scratch.
- * Norms are accumulated in float64; the sums run in row order (deterministic).
+ * Norms are accumulated in float64. sums[0..1] are formed in a fixed order: 256 interleaved partial
+ * sums (partial t adds rows t, t+256, t+512, ... in that order), then the 256 partials in order; the
+ * result is deterministic.
  * Errors: EINVAL (null outputs, rows < 0, d < 1). */
 int kvprof_compare(const float* o_q, const float* o_ref, const int32_t* top32_q,
                    const int32_t* top32_ref, int64_t rows, int32_t d, float* rel_l2_row,
@@ -211,7 +231,8 @@ int kvprof_compare(const float* o_q, const float* o_ref, const int32_t* top32_q,
  *   a, b      device float32 [rows][d]; cos_row  device float32 [rows]
  *   sums      device double [3 + 3*rows]: sums[0] = sum_i a_i.b_i, sums[1] = sum_i |a_i|^2,
  *             sums[2] = sum_i |b_i|^2 (tensor-level cosine = sums[0] / sqrt(sums[1] sums[2])); the
- *             remaining 3*rows entries are scratch. Sums run in row order (deterministic).
+ *             remaining 3*rows entries are scratch. The sums use the fixed interleaved order of
+ *             kvprof_compare (256 partials over rows t, t+256, ..., then the partials in order).
  * Errors: EINVAL (rows < 0, d < 1, null pointers), EALIGN (sums not 8-byte aligned). */
 int kvprof_ablation_bias(const float* key_bias, int32_t n_k, int32_t drop_lo, int32_t drop_hi, float* out,
                          void* stream);

@@ -112,7 +112,16 @@ def _check(fn: str, status: int):
 
 
 def _ptr(t) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor argument. The library reads and writes every array as dense memory
+    on the GPU, so a host tensor or a strided view is refused here, before any call reaches it."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise KvprofError("binding", KVPROF_EINVAL, f"tensor on {t.device}: the library needs GPU memory")
+    if not t.is_contiguous():
+        raise KvprofError("binding", KVPROF_EINVAL,
+                          f"tensor of shape {tuple(t.shape)} and strides {t.stride()} is not contiguous")
+    return t.data_ptr()
 
 
 def _stream(stream=None) -> Optional[int]:
@@ -261,7 +270,8 @@ def kvprof_ablation_bias(n_k: int, drop, key_bias=None, device=None, stream=None
     """Key bias that drops keys [lo, hi) (local output ablation); returns a float32 [n_k] tensor."""
     import torch
 
-    dev = key_bias.device if key_bias is not None else device
+    dev = key_bias.device if key_bias is not None else (device if device is not None else
+                                                         torch.device("cuda", torch.cuda.current_device()))
     out = torch.empty(n_k, dtype=torch.float32, device=dev)
     _check("kvprof_ablation_bias", load().kvprof_ablation_bias(_ptr(key_bias), n_k, int(drop[0]), int(drop[1]),
                                                                _ptr(out), _stream(stream)))

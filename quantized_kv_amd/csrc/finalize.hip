@@ -115,7 +115,8 @@ __global__ __launch_bounds__(64) void compare_kernel(const float* __restrict__ o
   }
 }
 
-// Single block: sums of the per-row partials in row order (deterministic).
+// Single block, fixed order: thread t sums rows t, t + 256, ... in turn, then thread 0 adds the 256
+// partial sums in order (deterministic).
 __global__ __launch_bounds__(256) void compare_sum_kernel(const double* __restrict__ part, long long rows,
                                                           double* __restrict__ sums) {
   __shared__ double sd[256], sn[256];

@@ -99,6 +99,7 @@ def check_rows(gpu, ref, rows=None, masses=True):
     if "top32" in gpu:
         idx = np.arange(len(n)) if rows is None else None
         check_top32(gpu["top32"][sl], ref["scores"][sl], n)
+        check_order(np.asarray(gpu["top32"][sl]), ref["scores"][sl], n)
     if "strict_zero" in gpu:
         check_strict_zero(gpu["strict_zero"][sl], ref["scores"][sl], n)
     if "o" in gpu and "o" in ref:

@@ -139,3 +139,78 @@ def test_ablation_entry_points_validate(lib):
     assert lib.kvprof_cosine(None, None, 4, 0, None, None, None) == B.KVPROF_EINVAL
     assert lib.kvprof_cosine(None, fake, 4, 128, fake, fake, None) == B.KVPROF_EINVAL
     assert lib.kvprof_cosine(fake, fake, 4, 128, fake, ctypes.c_void_p(260), None) == B.KVPROF_EALIGN
+
+
+def test_binding_refuses_host_and_strided_tensors():
+    """The binding passes device addresses only: a host tensor or a non-contiguous view is refused
+    before any library call (the library would otherwise read or write it as dense GPU memory)."""
+    import torch
+
+    with pytest.raises(B.KvprofError, match="GPU memory"):
+        B._ptr(torch.zeros(4))
+
+    class _StridedDeviceView:  # stands in for a CUDA view on a machine without a GPU
+        is_cuda = True
+        shape = (4, 2)
+        device = "cuda:0"
+
+        def is_contiguous(self):
+            return False
+
+        def stride(self):
+            return (4, 2)
+
+        def data_ptr(self):
+            raise AssertionError("address taken from a strided view")
+
+    with pytest.raises(B.KvprofError, match="not contiguous"):
+        B._ptr(_StridedDeviceView())
+    q = torch.zeros((1, 1, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(B.KvprofError, match="GPU memory"):
+        B.run(q, q, want=("support",))
+
+
+# The calls the boundary exports and their parameter types, as declared in include/kvprof.h. These are
+# the survey's proposed calls with its two deliberate departures: bf16-only inputs (no dtype argument)
+# and dense rows (no leading dimension), and the stream passed as void*.
+_SIGNATURES = {
+    "kvprof_abi_version": ("int", ["void"]),
+    "kvprof_last_error": ("const char*", ["void"]),
+    "kvprof_pack_mxfp8": ("int", ["const uint16_t*", "int64_t", "int32_t", "const int8_t*", "uint8_t*",
+                                  "uint8_t*", "void*"]),
+    "kvprof_unpack_mxfp8": ("int", ["const uint8_t*", "const uint8_t*", "int64_t", "int32_t", "float*",
+                                    "void*"]),
+    "kvprof_int4kv_bytes": ("size_t", ["int64_t", "int32_t", "int32_t"]),
+    "kvprof_pack_int4kv": ("int", ["const uint16_t*", "const uint16_t*", "int32_t", "int64_t", "int32_t",
+                                   "int32_t", "void*", "size_t", "void*"]),
+    "kvprof_unpack_int4kv": ("int", ["const void*", "int32_t", "int64_t", "int32_t", "int32_t", "float*",
+                                     "float*", "void*"]),
+    "kvprof_workspace_bytes": ("size_t", ["const kvprof_args*"]),
+    "kvprof_row_stats": ("int", ["const kvprof_args*", "void*"]),
+    "kvprof_attend": ("int", ["const kvprof_args*", "void*"]),
+}
+
+
+def _declarations():
+    import re
+
+    txt = open(B.HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+    out = {}
+    for m in re.finditer(r"((?:const\s+)?\w+\s*\*?)\s*(kvprof_\w+)\s*\(([^)]*)\)\s*;", txt):
+        ret = m.group(1).replace(" ", "").replace("constchar", "const char")
+        params = []
+        for p in m.group(3).split(","):
+            p = " ".join(p.split())
+            if p != "void":
+                p = re.sub(r"\s*(\w+)$", "", p)  # drop the parameter name
+            params.append(p.replace(" *", "*"))
+        out[m.group(2)] = (ret, params)
+    return out
+
+
+def test_declared_signatures_match_the_boundary_list():
+    decl = _declarations()
+    for name, (ret, params) in _SIGNATURES.items():
+        assert name in decl, name
+        assert decl[name] == (ret, params), (name, decl[name])
