@@ -199,6 +199,21 @@ int kvprof_row_stats(const kvprof_args* a, void* stream);
  * indices and region masses give recall@32 and the recent-window mass). o is required. */
 int kvprof_attend(const kvprof_args* a, void* stream);
 
+/* Allocation-free variant of kvprof_row_stats, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). It takes the same
+ * arguments and produces the same results with the same kernels, but ignores a->workspace and
+ * a->workspace_bytes: its scratch space is a fixed device array inside the library, of
+ * kvprof_noalloc_scratch_bytes() bytes (32 MiB) on every GPU the library runs on, held until the
+ * process ends. The call allocates nothing (no hipMalloc, no library allocation). Calls whose
+ * kvprof_workspace_bytes() exceeds that size fail with KVPROF_ESIZE before any device work.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (on different
+ * streams or host threads) race and must be serialised by the caller. The array keeps the last call's
+ * contents; the kernels clear what must start at zero themselves.
+ * Errors: those of kvprof_row_stats, ESIZE as above, ELAUNCH if the array's device address cannot be
+ * obtained. */
+int kvprof_row_stats_noalloc(const kvprof_args* a, void* stream);
+size_t kvprof_noalloc_scratch_bytes(void);
+
 /* Compare two attention outputs row by row ("KV residual window": relative L2 of the output; the
  * predictor study, section 0: recall@32).
  *   o_q, o_ref     float32 [rows][d];  top32_q, top32_ref  int32 [rows][32] (or both NULL)

@@ -87,11 +87,15 @@ def load(path: str = LIB_PATH):
     lib.kvprof_workspace_bytes.argtypes = [ctypes.POINTER(KvprofArgs)]
     lib.kvprof_row_stats.argtypes = [ctypes.POINTER(KvprofArgs), _P]
     lib.kvprof_attend.argtypes = [ctypes.POINTER(KvprofArgs), _P]
+    lib.kvprof_row_stats_noalloc.argtypes = [ctypes.POINTER(KvprofArgs), _P]
+    lib.kvprof_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.kvprof_noalloc_scratch_bytes.argtypes = []
     lib.kvprof_compare.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]
     lib.kvprof_ablation_bias.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
     lib.kvprof_cosine.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]
     for name in ("kvprof_pack_mxfp8", "kvprof_unpack_mxfp8", "kvprof_pack_int4kv",
-                 "kvprof_unpack_int4kv", "kvprof_row_stats", "kvprof_attend", "kvprof_compare",
+                 "kvprof_unpack_int4kv", "kvprof_row_stats", "kvprof_attend", "kvprof_row_stats_noalloc",
+                 "kvprof_compare",
                  "kvprof_ablation_bias", "kvprof_cosine"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -253,6 +257,15 @@ def kvprof_attend(args: KvprofArgs, stream=None):
     _check("kvprof_attend", load().kvprof_attend(ctypes.byref(args), _stream(stream)))
 
 
+def kvprof_row_stats_noalloc(args: KvprofArgs, stream=None):
+    """kvprof_row_stats with the library's fixed device scratch instead of args.workspace."""
+    _check("kvprof_row_stats_noalloc", load().kvprof_row_stats_noalloc(ctypes.byref(args), _stream(stream)))
+
+
+def kvprof_noalloc_scratch_bytes() -> int:
+    return int(load().kvprof_noalloc_scratch_bytes())
+
+
 def kvprof_compare(o_q, o_ref, top32_q=None, top32_ref=None, stream=None):
     """Per-row relative L2 and recall@32, plus the two sums of the tensor-level relative L2."""
     import torch
@@ -290,7 +303,7 @@ def kvprof_cosine(a, b, stream=None):
 
 
 def run(q, k=None, v=None, *, want=("support", "top_mass", "top32", "strict_zero", "row_max", "row_lse"),
-        attend=False, heatmap=False, hist=False, stream=None, **kw):
+        attend=False, heatmap=False, hist=False, noalloc=False, stream=None, **kw):
     """Allocate the requested outputs (and the workspace), call kvprof_row_stats (or kvprof_attend),
     and return the outputs as a dict of torch tensors (not synchronised)."""
     import torch
@@ -310,11 +323,15 @@ def run(q, k=None, v=None, *, want=("support", "top_mass", "top32", "strict_zero
         kw.setdefault("hist_bins", 100)
         hs = torch.empty((B, 1 + n_regions, kw["hist_bins"]), dtype=torch.int32, device=q.device)
     args = make_args(q, k, v, outputs=outs, heatmap=hm, heatmap_mean=hm_mean, hist=hs, **kw)
-    nws = kvprof_workspace_bytes(args)
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device) if nws else None
-    if ws is not None:
-        args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
-    (kvprof_attend if attend else kvprof_row_stats)(args, stream)
+    ws = None
+    if noalloc:  # the library's own device scratch: no workspace tensor
+        kvprof_row_stats_noalloc(args, stream)
+    else:
+        nws = kvprof_workspace_bytes(args)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device) if nws else None
+        if ws is not None:
+            args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+        (kvprof_attend if attend else kvprof_row_stats)(args, stream)
     res = dict(outs)
     if hm is not None:
         res["heatmap"], res["heatmap_mean"] = hm, hm_mean

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kvprof_internal.h"
@@ -295,6 +296,34 @@ int run_rows(const kvprof_args* a, void* stream, bool need_o) {
   return ok();
 }
 
+// ---- device scratch of the allocation-free entry point -------------------------------------------
+// A file-scope device array: each GPU the library runs on holds one copy until the process ends. In host
+// code its name is only a stand-in, never a device address; the address comes from hipGetSymbolAddress,
+// taken once per device with that device current and kept per device.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVPROF_ELAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVPROF_EUNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(KVPROF_ELAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVPROF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -368,6 +397,27 @@ size_t kvprof_workspace_bytes(const kvprof_args* a) {
 int kvprof_row_stats(const kvprof_args* a, void* stream) { return run_rows(a, stream, false); }
 
 int kvprof_attend(const kvprof_args* a, void* stream) { return run_rows(a, stream, true); }
+
+size_t kvprof_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int kvprof_row_stats_noalloc(const kvprof_args* a, void* stream) {
+  if (!a) return fail(KVPROF_EINVAL, "null argument struct");
+  kvprof_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  const size_t need = workspace_layout(&b).total;
+  if (need > kScratchBytes)
+    return fail(KVPROF_ESIZE, "these arguments need %zu bytes of scratch; the allocation-free entry point holds %zu",
+                need, kScratchBytes);
+  int st = validate_args(&b, false);  // every argument check except the workspace, before any device call
+  if (st != KVPROF_OK && st != KVPROF_ESIZE) return st;
+  void* ptr = nullptr;
+  st = scratch_of_current_device(&ptr);
+  if (st != KVPROF_OK) return st;
+  b.workspace = ptr;
+  b.workspace_bytes = kScratchBytes;
+  return run_rows(&b, stream, false);
+}
 
 int kvprof_compare(const float* o_q, const float* o_ref, const int32_t* top32_q, const int32_t* top32_ref,
                    int64_t rows, int32_t d, float* rel_l2_row, float* recall_row, double* sums, void* stream) {

@@ -214,3 +214,17 @@ def test_declared_signatures_match_the_boundary_list():
     for name, (ret, params) in _SIGNATURES.items():
         assert name in decl, name
         assert decl[name] == (ret, params), (name, decl[name])
+
+
+def test_noalloc_rejects_oversized_scratch_before_device_work(lib):
+    """The allocation-free entry point refuses arguments whose scratch exceeds its fixed array, before
+    any device call (so this runs without a GPU), and validates like kvprof_row_stats."""
+    assert lib.kvprof_noalloc_scratch_bytes() == 32 << 20
+    a = _args(mode=B.MODE_MXFP8, n_batch=8, n_heads_q=32, n_heads_kv=32, n_q=96, n_k=6240,
+              q_codes=1, q_scales=1, k_codes=1, k_scales=1)
+    assert lib.kvprof_workspace_bytes(ctypes.byref(a)) > (32 << 20)
+    assert lib.kvprof_row_stats_noalloc(ctypes.byref(a), None) == B.KVPROF_ESIZE
+    assert "allocation-free" in _err(lib)
+    assert lib.kvprof_row_stats_noalloc(None, None) == B.KVPROF_EINVAL
+    a = _args(d=64)
+    assert lib.kvprof_row_stats_noalloc(ctypes.byref(a), None) == B.KVPROF_ESHAPE
