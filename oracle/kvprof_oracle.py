@@ -9,6 +9,7 @@ Each function restates a definition from the pages, cited by page title and sect
 
 * P1 = "Catnip Week 10 KV Cache Attention Study" (cappuccino.cafe/kv-attn.html)
 * P2 = "KV residual window" (huhohoo.com/zh-TW/docs/llm/kv-residual-window)
+* P3 = the run manifest of the fine-grained per-head KV-cache analysis (cappuccino.cafe/kv-fine.html)
 * P4 = the MiniCPM5-2B attention-predictor study (bjdmk.com.cn/news/5855973)
 
 Where a page is silent the reading taken is stated at the function; every reading is also listed
@@ -538,3 +539,90 @@ def ablation_metrics(o_abl: np.ndarray, o_full: np.ndarray) -> dict:
     ff = np.asarray(o_full, dtype=np.float64).ravel()
     return {"rel_l2_row": rel_l2_rows(o_abl, o_full), "cos_row": cosine_rows(o_abl, o_full),
             "rel_l2": rel_l2(fa, ff), "cos": float(fa @ ff) / (np.linalg.norm(fa) * np.linalg.norm(ff))}
+
+
+# ----------------------------------------------------------------------------------------------
+# Spatial heatmaps (P1 "Temporal & spatial heatmaps": Figure 9, region spatial maps normalised inside
+# each region; Figure 10, a representative query's per-key-frame 15x26 maps with the colour range
+# clipped at the record's 99.5th percentile. P3, the run manifest's config block: a 64x96 heatmap pool
+# shape and a cap of 65,536 values on the sample a quantile statistic is taken over.)
+# ----------------------------------------------------------------------------------------------
+
+QUANTILE_SAMPLE_CAP = 65536
+POOL_SHAPE = (64, 96)
+
+
+def region_spatial_maps(p_rows: np.ndarray, region_bounds, frame_len: int) -> np.ndarray:
+    """Key spatial preference inside each region, pooled over the given rows.
+
+    Key j sits at latent-grid cell j mod frame_len of its frame. For region [a, b):
+    map[c] = (sum over rows and over keys j in [a, b) with j mod frame_len = c of p_j) / (sum over rows
+    of the region's mass). Reading: the rows' probabilities are pooled before the normalisation (the
+    map of the rows' mean attention restricted to the region), so each map sums to 1; a region with no
+    mass gives an all-zero map. Returns [n_regions, frame_len].
+    """
+    p = np.asarray(p_rows, dtype=np.float64)
+    b = list(region_bounds)
+    out = np.zeros((len(b) - 1, frame_len))
+    for q in range(len(b) - 1):
+        for j in range(b[q], b[q + 1]):
+            out[q, j % frame_len] += float(np.sum(p[:, j]))
+        tot = float(np.sum(out[q]))
+        if tot > 0:
+            out[q] /= tot
+    return out
+
+
+def percentile_linear(values: np.ndarray, pct: float) -> float:
+    """The pct-th percentile with linear interpolation between order statistics: sort ascending,
+    position pos = (n - 1) pct / 100, value = v[floor(pos)] + frac(pos) (v[floor(pos) + 1] - v[floor(pos)])."""
+    v = np.sort(np.asarray(values, dtype=np.float64).ravel())
+    pos = (v.size - 1) * pct / 100.0
+    lo = int(math.floor(pos))
+    hi = min(lo + 1, v.size - 1)
+    return float(v[lo] + (pos - lo) * (v[hi] - v[lo]))
+
+
+def quantile_sample(values: np.ndarray, cap: int = QUANTILE_SAMPLE_CAP) -> np.ndarray:
+    """At most `cap` values for a quantile statistic. Reading: all values when there are no more than
+    cap of them, otherwise every ceil(n / cap)-th value in index order (a fixed stride, so the sample is
+    reproducible)."""
+    v = np.asarray(values).ravel()
+    if v.size <= cap:
+        return v
+    return v[:: -(-v.size // cap)]
+
+
+def key_frame_heatmaps(p_row: np.ndarray, frame_len: int, n_frames: int, pct: float = 99.5):
+    """A query's probabilities as n_frames maps of frame_len cells, clipped at the pct-th percentile of
+    the record's values (Figure 10). Reading: the record is the representative query's own
+    n_frames x frame_len values. Returns (maps [n_frames, frame_len] = min(p, clip), clip)."""
+    p = np.asarray(p_row, dtype=np.float64)[: n_frames * frame_len].reshape(n_frames, frame_len)
+    clip = percentile_linear(quantile_sample(p), pct)
+    return np.minimum(p, clip), clip
+
+
+def pooled_map(a: np.ndarray, shape=POOL_SHAPE) -> np.ndarray:
+    """Adaptive average pooling of a [M, N] attention map to shape (H, W): cell (i, j) is the mean of
+    a[floor(i M / H) : ceil((i + 1) M / H), floor(j N / W) : ceil((j + 1) N / W)]."""
+    a = np.asarray(a, dtype=np.float64)
+    M, N = a.shape
+    H, W = shape
+    out = np.zeros((H, W))
+    for i in range(H):
+        r0, r1 = (i * M) // H, -(-((i + 1) * M) // H)
+        for j in range(W):
+            c0, c1 = (j * N) // W, -(-((j + 1) * N) // W)
+            out[i, j] = float(np.mean(a[r0:r1, c0:c1]))
+    return out
+
+
+def key_mass(p_rows: np.ndarray) -> np.ndarray:
+    """Attention mass each key receives from a set of rows: sum over the rows of p_j."""
+    return np.sum(np.asarray(p_rows, dtype=np.float64), axis=0)
+
+
+def probabilities(q, k, *, scale, key_bias=None, causal=False, q_pos0=0) -> np.ndarray:
+    """The softmax probability matrix [Mq, Sk] of one head (invisible keys 0)."""
+    s = scores(q, k, scale, key_bias, causal, q_pos0)
+    return np.stack([softmax_row(s[i]) for i in range(s.shape[0])])
