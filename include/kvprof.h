@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define KVPROF_ABI_VERSION 1
+#define KVPROF_ABI_VERSION 2
 
 /* Status codes. */
 #define KVPROF_OK 0
@@ -67,6 +67,7 @@ extern "C" {
 #define KVPROF_MAX_KEYS_MX 6400  /* keys per row in MXFP8 mode (8 waves x 50 tiles)                    */
 #define KVPROF_MAX_REGIONS 8
 #define KVPROF_MAX_FRAMES 64
+#define KVPROF_MAX_POOL_W 128    /* widest pooled probability map                                     */
 
 int kvprof_abi_version(void);
 
@@ -168,6 +169,23 @@ typedef struct kvprof_args {
   uint32_t* hist;               /* [n_batch][1+n_regions][hist_bins]: support, then each region mass; */
                                 /*   bin = min(floor(100 x), 99). Accumulated with atomics: the call  */
                                 /*   clears it first.                                                  */
+  /* Probability maps, BF16 mode only ("Catnip Week 10 KV Cache Attention Study", section "Temporal & */
+  /* spatial heatmaps": Figure 9's region-normalised key spatial maps, Figure 10's per-query maps; the */
+  /* run manifest of the fine-grained per-head analysis, config block: the heatmap pool shape). A    */
+  /* second pass over K after the row statistics, with p_ij = exp(s_ij - lse_i).                      */
+  float* key_mass;              /* [n_batch][n_heads_q][n_k] sum over the head's n_q queries of p_j   */
+  float* spatial;               /* [n_batch][n_heads_q][n_regions][frame_len] key spatial maps: cell c*/
+                                /*   of region q = mass of the region's keys j with j mod frame_len =  */
+                                /*   c, over the region's mass (all 0 when the region has none)        */
+  float* spatial_mean;          /* [n_batch][n_regions][frame_len] the same over all query heads'     */
+                                /*   summed key masses                                                 */
+  int32_t pool_h, pool_w;       /* shape of `pooled`: pool_h >= 1, 1 <= pool_w <= KVPROF_MAX_POOL_W    */
+  float* pooled;                /* [n_batch][n_heads_q][pool_h][pool_w] adaptive average pooling of   */
+                                /*   each head's [n_q][n_k] probability matrix: cell (i, c) = mean of p */
+                                /*   over rows [floor(i n_q/pool_h), ceil((i+1) n_q/pool_h)) x keys     */
+                                /*   [floor(c n_k/pool_w), ceil((c+1) n_k/pool_w)) (invisible keys 0)   */
+  int64_t p_row;                /* row (global index) whose probabilities are copied to p_row_out     */
+  float* p_row_out;             /* [n_k] p of row p_row (invisible keys 0), or NULL for none          */
   void* workspace;              /* device scratch of at least kvprof_workspace_bytes(args) bytes,     */
   size_t workspace_bytes;       /*   256-byte aligned (may be NULL when that size is 0)                */
 } kvprof_args;
@@ -177,8 +195,10 @@ typedef struct kvprof_args {
  *  Study", experiment design, GPU-side reduction — so intermediate state stays in this device buffer.)
  * Every call with at least one row needs some: a list of the 16-row blocks whose exact ranks take
  * the slow path (4 bytes per block + 4), plus the decoded MXFP8 operands and, for heatmaps or
- * histograms requested without their per-row inputs, those per-row arrays. The contents need no
- * initialisation; concurrent calls must not share a workspace. */
+ * histograms requested without their per-row inputs, those per-row arrays; for the probability maps,
+ * per-32-row-block key masses (key_mass, spatial, spatial_mean), per-row pooled window sums (pooled)
+ * and row_lse / key_mass when not requested. The contents need no initialisation; concurrent calls
+ * must not share a workspace. */
 size_t kvprof_workspace_bytes(const kvprof_args* a);
 
 /* Row statistics over bf16 or MXFP8 scores (modes BF16 and MXFP8), optionally with O = P.V.
@@ -188,8 +208,10 @@ size_t kvprof_workspace_bytes(const kvprof_args* a);
  *  probability quantization for TV, argmax agreement and the P-path. Top-32 indices: the MiniCPM5-2B
  *  predictor study, section 0.)
  * Requires d == 128 and n_k <= KVPROF_MAX_KEYS (KVPROF_MAX_KEYS_MX in MXFP8 mode).
+ * The probability maps (key_mass ... p_row_out) need BF16 mode; spatial and spatial_mean need
+ * n_regions > 0 and frame_len > 0.
  * Errors: EINVAL, ESHAPE, EALIGN (q, k, v, codes not 16-byte aligned), ESIZE (workspace),
- * EUNSUPPORTED (n_k or region/frame counts beyond the limits), ELAUNCH. */
+ * EUNSUPPORTED (n_k or region/frame counts beyond the limits, maps outside BF16 mode), ELAUNCH. */
 int kvprof_row_stats(const kvprof_args* a, void* stream);
 
 /* ("KV residual window": the output of attention over the dequantized cache and its relative L2; the
@@ -198,6 +220,22 @@ int kvprof_row_stats(const kvprof_args* a, void* stream);
  * 4-bit K/V with the float32 recent window (mode INT4KV), with any of the row statistics (the top-32
  * indices and region masses give recall@32 and the recent-window mass). o is required. */
 int kvprof_attend(const kvprof_args* a, void* stream);
+
+/* Colour-range clip of a heatmap ("Catnip Week 10 KV Cache Attention Study", Figure 10: maps clipped at
+ * the record's 99.5th percentile; the run manifest of the fine-grained per-head analysis, config block:
+ * a quantile statistic is taken over at most 65,536 values).
+ *   x     device float32 [n], n >= 1, no NaN.
+ *   pct   percentile in [0, 100].
+ *   cap   sample limit >= 1: all n values when n <= cap, else x[0], x[s], x[2s], ... with
+ *         s = ceil(n / cap) (m = ceil(n / s) values).
+ *   clip  device float32 [1]: with the m sampled values sorted ascending as v, pos = (m - 1) * pct / 100
+ *         in float64, lo = floor(pos), hi = min(lo + 1, m - 1): v[lo] + (pos - lo) * (v[hi] - v[lo])
+ *         in float64, rounded to float32 (linear interpolation between order statistics).
+ *   y     device float32 [n] = min(x, clip) elementwise, or NULL. y may equal x.
+ * Errors: EINVAL (n < 1, cap < 1, pct outside [0, 100] or not finite, null x or clip), EALIGN (arrays not
+ * 4-byte aligned). */
+int kvprof_percentile_clip(const float* x, int64_t n, double pct, int64_t cap, float* clip, float* y,
+                           void* stream);
 
 /* Allocation-free variant of kvprof_row_stats, for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). It takes the same

@@ -57,6 +57,9 @@ class KvprofArgs(ctypes.Structure):
         ("tv_qk", _P), ("argmax", _P), ("argmax_ref", _P), ("p_zero_frac", _P), ("tv_p", _P),
         ("p_rowsum", _P),
         ("heatmap", _P), ("heatmap_mean", _P), ("hist", _P),
+        ("key_mass", _P), ("spatial", _P), ("spatial_mean", _P),
+        ("pool_h", ctypes.c_int32), ("pool_w", ctypes.c_int32), ("pooled", _P),
+        ("p_row", ctypes.c_int64), ("p_row_out", _P),
         ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -93,10 +96,11 @@ def load(path: str = LIB_PATH):
     lib.kvprof_compare.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]
     lib.kvprof_ablation_bias.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
     lib.kvprof_cosine.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]
+    lib.kvprof_percentile_clip.argtypes = [_P, ctypes.c_int64, ctypes.c_double, ctypes.c_int64, _P, _P, _P]
     for name in ("kvprof_pack_mxfp8", "kvprof_unpack_mxfp8", "kvprof_pack_int4kv",
                  "kvprof_unpack_int4kv", "kvprof_row_stats", "kvprof_attend", "kvprof_row_stats_noalloc",
                  "kvprof_compare",
-                 "kvprof_ablation_bias", "kvprof_cosine"):
+                 "kvprof_ablation_bias", "kvprof_cosine", "kvprof_percentile_clip"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -302,10 +306,27 @@ def kvprof_cosine(a, b, stream=None):
     return cos, sums[:3]
 
 
+QUANTILE_SAMPLE_CAP = 65536
+
+
+def kvprof_percentile_clip(x, pct=99.5, cap=QUANTILE_SAMPLE_CAP, clipped=True, stream=None):
+    """Percentile of a float32 tensor's values (over the capped sample) and, with clipped=True, the
+    values clipped to it. Returns (clip float32 [1], y float32 like x or None)."""
+    import torch
+
+    clip = torch.empty(1, dtype=torch.float32, device=x.device)
+    y = torch.empty_like(x) if clipped else None
+    _check("kvprof_percentile_clip", load().kvprof_percentile_clip(_ptr(x), x.numel(), float(pct), int(cap),
+                                                                   _ptr(clip), _ptr(y), _stream(stream)))
+    return clip, y
+
+
 def run(q, k=None, v=None, *, want=("support", "top_mass", "top32", "strict_zero", "row_max", "row_lse"),
-        attend=False, heatmap=False, hist=False, noalloc=False, stream=None, **kw):
+        attend=False, heatmap=False, hist=False, noalloc=False, maps_want=(), pool=None, p_row=None,
+        stream=None, **kw):
     """Allocate the requested outputs (and the workspace), call kvprof_row_stats (or kvprof_attend),
-    and return the outputs as a dict of torch tensors (not synchronised)."""
+    and return the outputs as a dict of torch tensors (not synchronised). maps_want names the key-mass
+    / spatial outputs, pool=(H, W) asks for the pooled map and p_row for one row's probabilities."""
     import torch
 
     B, Hq, Mq, _ = q.shape
@@ -322,7 +343,26 @@ def run(q, k=None, v=None, *, want=("support", "top_mass", "top32", "strict_zero
     if hist:
         kw.setdefault("hist_bins", 100)
         hs = torch.empty((B, 1 + n_regions, kw["hist_bins"]), dtype=torch.int32, device=q.device)
+    maps = {}
+    if maps_want:
+        # probability maps: key_mass, spatial, spatial_mean, pooled (shape pool=(H, W)), p_row (index)
+        n_k = k.shape[2] if k is not None else kw["n_k"]
+        fl = kw.get("frame_len", 0)
+        shapes = {"key_mass": (B, Hq, n_k), "spatial": (B, Hq, n_regions, fl), "spatial_mean": (B, n_regions, fl)}
+        for name in maps_want:
+            if name in shapes:
+                maps[name] = torch.empty(shapes[name], dtype=torch.float32, device=q.device)
+        if pool is not None:
+            maps["pooled"] = torch.empty((B, Hq) + tuple(pool), dtype=torch.float32, device=q.device)
+        if p_row is not None:
+            maps["p_row_out"] = torch.empty(n_k, dtype=torch.float32, device=q.device)
     args = make_args(q, k, v, outputs=outs, heatmap=hm, heatmap_mean=hm_mean, hist=hs, **kw)
+    for name, t in maps.items():
+        setattr(args, name, _ptr(t))
+    if pool is not None:
+        args.pool_h, args.pool_w = int(pool[0]), int(pool[1])
+    if p_row is not None:
+        args.p_row = int(p_row)
     ws = None
     if noalloc:  # the library's own device scratch: no workspace tensor
         kvprof_row_stats_noalloc(args, stream)
@@ -333,6 +373,7 @@ def run(q, k=None, v=None, *, want=("support", "top_mass", "top32", "strict_zero
             args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
         (kvprof_attend if attend else kvprof_row_stats)(args, stream)
     res = dict(outs)
+    res.update(maps)
     if hm is not None:
         res["heatmap"], res["heatmap_mean"] = hm, hm_mean
     if hs is not None:

@@ -55,10 +55,14 @@ int check_mx_shape(const void* x, const void* codes, const void* scales, int64_t
 }
 
 struct Workspace {
-  size_t q_mx = 0, k_mx = 0, frame = 0, support = 0, region = 0, redo = 0, total = 0;
+  size_t q_mx = 0, k_mx = 0, frame = 0, support = 0, region = 0, redo = 0;
+  size_t lse = 0, kpart = 0, kmass = 0, ppart = 0, total = 0;
 };
 
 int64_t total_rows(const kvprof_args* a) { return (int64_t)a->n_batch * a->n_heads_q * a->n_q; }
+
+bool wants_key_mass(const kvprof_args* a) { return a->key_mass || a->spatial || a->spatial_mean; }
+bool wants_maps(const kvprof_args* a) { return wants_key_mass(a) || a->pooled || a->p_row_out; }
 
 Workspace workspace_layout(const kvprof_args* a) {
   Workspace w;
@@ -82,6 +86,24 @@ Workspace workspace_layout(const kvprof_args* a) {
     if (!a->region_mass && a->n_regions > 0) {
       w.region = off;
       off += round256((size_t)rows * a->n_regions * 4);
+    }
+  }
+  if (rows > 0 && wants_maps(a)) {  // probability maps
+    if (!a->row_lse) {
+      w.lse = off;
+      off += round256((size_t)rows * 4);
+    }
+    if (wants_key_mass(a)) {
+      w.kpart = off;
+      off += round256((size_t)kvp::map_blocks(a->n_batch, a->n_heads_q, a->n_q) * a->n_k * 4);
+      if (!a->key_mass) {
+        w.kmass = off;
+        off += round256((size_t)a->n_batch * a->n_heads_q * a->n_k * 4);
+      }
+    }
+    if (a->pooled && a->pool_w > 0) {
+      w.ppart = off;
+      off += round256((size_t)rows * a->pool_w * 4);
     }
   }
   if (rows > 0 && a->n_heads_kv > 0) {  // redo list of the row kernel
@@ -154,11 +176,23 @@ int validate_args(const kvprof_args* a, bool need_o) {
   if (a->heatmap && (!a->row_group || a->n_groups <= 0)) return fail(KVPROF_EINVAL, "heatmap needs row_group and n_groups > 0");
   if (a->hist_bins < 0 || a->hist_bins > 1024) return fail(KVPROF_EINVAL, "hist_bins must lie in [0, 1024]");
   if (a->hist && a->hist_bins == 0) return fail(KVPROF_EINVAL, "hist needs hist_bins > 0");
+  if (wants_maps(a)) {
+    if (a->mode != KVPROF_MODE_BF16) return fail(KVPROF_EUNSUPPORTED, "probability maps need BF16 mode");
+    if ((a->spatial || a->spatial_mean) && (a->n_regions == 0 || a->frame_len <= 0))
+      return fail(KVPROF_EINVAL, "spatial maps need n_regions > 0 and frame_len > 0");
+    if (a->pooled && (a->pool_h < 1 || a->pool_w < 1 || a->pool_w > KVPROF_MAX_POOL_W))
+      return fail(KVPROF_EINVAL, "pooled needs pool_h >= 1 and 1 <= pool_w <= %d (got %d x %d)", KVPROF_MAX_POOL_W,
+                  a->pool_h, a->pool_w);
+    if (a->pooled && a->n_q < 1) return fail(KVPROF_EINVAL, "pooled needs n_q >= 1");
+    if (a->p_row_out && (a->p_row < 0 || a->p_row >= rows))
+      return fail(KVPROF_EINVAL, "p_row %lld outside [0, %lld)", (long long)a->p_row, (long long)rows);
+  }
   const bool tvouts = a->tv_qk || a->argmax || a->argmax_ref || a->p_zero_frac || a->tv_p || a->p_rowsum;
   if (tvouts && a->mode != KVPROF_MODE_MXFP8) return fail(KVPROF_EINVAL, "TV / argmax / P-path outputs need MXFP8 mode");
   const void* outs[] = {a->support, a->top_mass, a->top32, a->strict_zero, a->region_mass, a->frame_mass,
                         a->row_max, a->row_lse, a->o, a->tv_qk, a->argmax, a->argmax_ref, a->p_zero_frac,
-                        a->tv_p, a->p_rowsum, a->heatmap, a->heatmap_mean, a->hist};
+                        a->tv_p, a->p_rowsum, a->heatmap, a->heatmap_mean, a->hist, a->key_mass,
+                        a->spatial, a->spatial_mean, a->pooled, a->p_row_out};
   for (const void* o : outs)
     if (o && !aligned(o, 4)) return fail(KVPROF_EALIGN, "outputs must be 4-byte aligned");
   const Workspace ws = workspace_layout(a);
@@ -218,8 +252,15 @@ int run_rows(const kvprof_args* a, void* stream, bool need_o) {
   st = build_segments(a, p, tpw);
   if (st != KVPROF_OK) return st;
   if (rows == 0) {
-    if (a->hist) return launched(kvp::launch_hist(nullptr, nullptr, a->n_batch, 0, a->n_regions, a->hist_bins, a->hist, s), "hist");
-    return ok();
+    hipError_t e0 = hipSuccess;
+    if (a->hist) e0 = kvp::launch_hist(nullptr, nullptr, a->n_batch, 0, a->n_regions, a->hist_bins, a->hist, s);
+    // no queries: every key receives no mass and every spatial map is zero
+    const long long nbh = (long long)a->n_batch * a->n_heads_q;
+    if (e0 == hipSuccess && a->key_mass) e0 = kvp::launch_zero_f32(a->key_mass, nbh * a->n_k, s);
+    if (e0 == hipSuccess && a->spatial) e0 = kvp::launch_zero_f32(a->spatial, nbh * a->n_regions * a->frame_len, s);
+    if (e0 == hipSuccess && a->spatial_mean)
+      e0 = kvp::launch_zero_f32(a->spatial_mean, (long long)a->n_batch * a->n_regions * a->frame_len, s);
+    return launched(e0, "empty problem");
   }
   const Workspace ws = workspace_layout(a);
   char* wsb = reinterpret_cast<char*>(a->workspace);
@@ -256,6 +297,8 @@ int run_rows(const kvprof_args* a, void* stream, bool need_o) {
   p.p_rowsum = a->p_rowsum;
   p.redo = reinterpret_cast<unsigned*>(wsb + ws.redo);
   if (a->heatmap && !a->frame_mass) p.frame_mass = reinterpret_cast<float*>(wsb + ws.frame);
+  const bool maps = wants_maps(a);
+  if (maps && !a->row_lse) p.row_lse = reinterpret_cast<float*>(wsb + ws.lse);
   if (a->hist) {
     if (!a->support) p.support = reinterpret_cast<float*>(wsb + ws.support);
     if (!a->region_mass && a->n_regions > 0) p.region_mass = reinterpret_cast<float*>(wsb + ws.region);
@@ -292,6 +335,40 @@ int run_rows(const kvprof_args* a, void* stream, bool need_o) {
     e = kvp::launch_hist(p.support, p.region_mass, a->n_batch, a->n_heads_q * a->n_q, a->n_regions,
                          a->hist_bins, a->hist, s);
     if (e != hipSuccess) return launched(e, "histogram");
+  }
+  if (maps) {
+    kvp::MapsParams mp;
+    std::memset(&mp, 0, sizeof(mp));
+    mp.n_batch = a->n_batch;
+    mp.n_heads_q = a->n_heads_q;
+    mp.n_heads_kv = a->n_heads_kv;
+    mp.n_q = a->n_q;
+    mp.n_k = a->n_k;
+    mp.group = a->n_heads_q / a->n_heads_kv;
+    mp.causal = a->causal;
+    mp.q_pos0 = a->q_pos0;
+    mp.scale_log2 = p.scale_log2;
+    mp.q = a->q;
+    mp.k = a->k;
+    mp.key_bias = a->key_bias;
+    mp.row_lse = p.row_lse;
+    float* key_mass = a->key_mass;
+    if (wants_key_mass(a)) {
+      mp.key_part = reinterpret_cast<float*>(wsb + ws.kpart);
+      if (!key_mass) key_mass = reinterpret_cast<float*>(wsb + ws.kmass);
+    }
+    if (a->pooled) {
+      mp.pool_part = reinterpret_cast<float*>(wsb + ws.ppart);
+      mp.pool_w = a->pool_w;
+    }
+    mp.p_row = a->p_row;
+    mp.p_row_out = a->p_row_out;
+    kvp::RegionBounds bounds;
+    std::memset(&bounds, 0, sizeof(bounds));
+    for (int i = 0; i <= a->n_regions && a->n_regions > 0; ++i) bounds.b[i] = a->region_bounds[i];
+    e = kvp::launch_maps(mp, bounds, key_mass, a->spatial, a->spatial_mean, a->n_regions, a->frame_len, a->pooled,
+                         a->pool_h, s);
+    if (e != hipSuccess) return launched(e, "probability maps");
   }
   return ok();
 }
@@ -417,6 +494,22 @@ int kvprof_row_stats_noalloc(const kvprof_args* a, void* stream) {
   b.workspace = ptr;
   b.workspace_bytes = kScratchBytes;
   return run_rows(&b, stream, false);
+}
+
+int kvprof_percentile_clip(const float* x, int64_t n, double pct, int64_t cap, float* clip, float* y,
+                           void* stream) {
+  if (n < 1 || cap < 1) return fail(KVPROF_EINVAL, "n and cap must be >= 1 (got %lld, %lld)", (long long)n, (long long)cap);
+  if (!std::isfinite(pct) || pct < 0.0 || pct > 100.0) return fail(KVPROF_EINVAL, "pct must lie in [0, 100]");
+  if (!x || !clip) return fail(KVPROF_EINVAL, "null pointer");
+  if (!aligned(x, 4) || !aligned(clip, 4) || (y && !aligned(y, 4))) return fail(KVPROF_EALIGN, "arrays must be 4-byte aligned");
+  const int64_t stride = n <= cap ? 1 : (n + cap - 1) / cap;
+  const int64_t m = (n + stride - 1) / stride;
+  const double pos = (double)(m - 1) * pct / 100.0;
+  const int64_t lo = (int64_t)std::floor(pos);
+  const int64_t hi = std::min<int64_t>(lo + 1, m - 1);
+  return launched(kvp::launch_percentile(x, n, stride, m, lo, hi, pos - (double)lo, clip, y,
+                                         reinterpret_cast<hipStream_t>(stream)),
+                  "percentile_clip");
 }
 
 int kvprof_compare(const float* o_q, const float* o_ref, const int32_t* top32_q, const int32_t* top32_ref,

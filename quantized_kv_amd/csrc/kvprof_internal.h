@@ -93,4 +93,40 @@ hipError_t launch_compare(const float* oq, const float* oref, const int* tq, con
                           int64_t rows, int d, float* rel_row, float* recall_row, double* sums,
                           hipStream_t s);
 
+// ---- probability maps (maps.hip) -------------------------------------------------------------------
+
+constexpr int kMaxPoolW = 128;  // widest pooled map (four 32-column MFMA blocks)
+
+struct MapsParams {
+  int n_batch, n_heads_q, n_heads_kv, n_q, n_k;
+  int group;  // n_heads_q / n_heads_kv
+  int causal;
+  long long q_pos0;
+  float scale_log2;  // scale * log2(e)
+  const uint16_t* q;  // bf16 [b][hq][nq][128]
+  const uint16_t* k;  // bf16 [b][hkv][nk][128]
+  const float* key_bias;
+  const float* row_lse;  // [rows] natural-log log-sum-exp of every row (from the row kernel)
+  float* key_part;       // [b][hq][ceil(nq/32)][nk] per-block key masses, or null
+  float* pool_part;      // [rows][pool_w] per-row sums over the pooled key windows, or null
+  int pool_w;
+  long long p_row;       // row copied to p_row_out (when that is not null)
+  float* p_row_out;
+};
+
+struct RegionBounds {
+  int b[KVPROF_MAX_REGIONS + 1];
+};
+
+inline long long map_blocks(int n_batch, int n_heads_q, int n_q) {
+  return (long long)n_batch * n_heads_q * ((n_q + 31) / 32);
+}
+
+hipError_t launch_maps(const MapsParams& p, const RegionBounds& bounds, float* key_mass, float* spatial,
+                       float* spatial_mean, int n_regions, int frame_len, float* pooled, int pool_h,
+                       hipStream_t s);
+hipError_t launch_zero_f32(float* x, long long n, hipStream_t s);
+hipError_t launch_percentile(const float* x, long long n, long long stride, long long m, long long lo,
+                             long long hi, double frac, float* clip, float* y, hipStream_t s);
+
 }  // namespace kvp

@@ -21,10 +21,10 @@ def test_exports_every_declared_symbol(lib):
     names = B.declared_functions()
     assert {"kvprof_pack_mxfp8", "kvprof_pack_int4kv", "kvprof_row_stats", "kvprof_attend",
             "kvprof_int4kv_bytes", "kvprof_compare", "kvprof_workspace_bytes", "kvprof_ablation_bias",
-            "kvprof_cosine"} <= set(names)
+            "kvprof_cosine", "kvprof_percentile_clip", "kvprof_row_stats_noalloc"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvprof_abi_version() == 1
+    assert lib.kvprof_abi_version() == 2
 
 
 def test_args_struct_layout_matches_header():
@@ -188,6 +188,8 @@ _SIGNATURES = {
     "kvprof_workspace_bytes": ("size_t", ["const kvprof_args*"]),
     "kvprof_row_stats": ("int", ["const kvprof_args*", "void*"]),
     "kvprof_attend": ("int", ["const kvprof_args*", "void*"]),
+    "kvprof_percentile_clip": ("int", ["const float*", "int64_t", "double", "int64_t", "float*", "float*",
+                                       "void*"]),
 }
 
 
@@ -228,3 +230,51 @@ def test_noalloc_rejects_oversized_scratch_before_device_work(lib):
     assert lib.kvprof_row_stats_noalloc(None, None) == B.KVPROF_EINVAL
     a = _args(d=64)
     assert lib.kvprof_row_stats_noalloc(ctypes.byref(a), None) == B.KVPROF_ESHAPE
+
+
+def test_maps_validation(lib):
+    """Probability-map arguments are checked on the host before anything is enqueued."""
+    fake = 0x10000
+    a = _args(mode=B.MODE_MXFP8, q_codes=1, q_scales=1, k_codes=1, k_scales=1)
+    a.key_mass = fake
+    assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_EUNSUPPORTED
+    assert "BF16" in _err(lib)
+    a = _args()
+    a.spatial = fake
+    assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_EINVAL  # no regions / frame_len
+    a = _args()
+    a.pooled, a.pool_h, a.pool_w = fake, 64, 129
+    assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_EINVAL
+    a.pool_w = 0
+    assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_EINVAL
+    a = _args()
+    a.p_row_out, a.p_row = fake, a.n_batch * a.n_heads_q * a.n_q
+    assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_EINVAL
+    a.p_row = -1
+    assert lib.kvprof_row_stats(ctypes.byref(a), None) == B.KVPROF_EINVAL
+
+
+def test_maps_workspace_sizes(lib):
+    a = _args(n_batch=1, n_heads_q=32, n_heads_kv=32, n_q=96, n_k=6240)
+    base = lib.kvprof_workspace_bytes(ctypes.byref(a))
+    a.key_mass = 0x10000
+    blocks = 32 * 3  # 32-row blocks
+    assert lib.kvprof_workspace_bytes(ctypes.byref(a)) == base + _r256(32 * 96 * 4) + _r256(blocks * 6240 * 4)
+    a.pooled, a.pool_h, a.pool_w = 0x10000, 64, 96
+    assert lib.kvprof_workspace_bytes(ctypes.byref(a)) == (base + _r256(32 * 96 * 4) + _r256(blocks * 6240 * 4)
+                                                         + _r256(32 * 96 * 96 * 4))
+
+
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_percentile_clip_validation(lib):
+    fake = ctypes.c_void_p(0x10000)
+    f = lib.kvprof_percentile_clip
+    assert f(fake, 0, 99.5, 65536, fake, None, None) == B.KVPROF_EINVAL
+    assert f(fake, 10, 100.5, 65536, fake, None, None) == B.KVPROF_EINVAL
+    assert f(fake, 10, float("nan"), 65536, fake, None, None) == B.KVPROF_EINVAL
+    assert f(fake, 10, 99.5, 0, fake, None, None) == B.KVPROF_EINVAL
+    assert f(None, 10, 99.5, 8, fake, None, None) == B.KVPROF_EINVAL
+    assert f(ctypes.c_void_p(0x10002), 10, 99.5, 8, fake, None, None) == B.KVPROF_EALIGN
