@@ -466,6 +466,69 @@ def unpack_int4kv(blob: np.ndarray):
     return np.concatenate([k_hat, kr]), np.concatenate([v_hat, vr])
 
 
+def rolled_window(r_in: int, n_new: int, r_window: int) -> int:
+    """Residual length after appending n_new tokens to a window of r_in float32 tokens when the oldest
+    residual tokens move to the 4-bit part in whole 32-token groups. Reading (P2 "適用邊界" names KIVI's
+    residual mechanism as what the static study leaves out): the window keeps at least the last
+    r_window tokens in float32, and once it holds r_window + 32 or more, its oldest tokens move in whole
+    groups, so afterwards it holds between r_window and r_window + 31 tokens. Below r_window + 32 nothing
+    moves."""
+    r = r_in + n_new
+    if r < r_window + INT4_GROUP:
+        return r
+    return r - INT4_GROUP * ((r - r_window) // INT4_GROUP)
+
+
+def int4kv_append(blob: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, r_window: int) -> np.ndarray:
+    """Append tokens (k_new, v_new: [t, d] bf16 values) to one packed head with rolling re-quantisation:
+    the new tokens join the float32 window; then, while the window holds more than needed (see
+    rolled_window), its oldest 32 tokens become one more K group (per channel over the 32 tokens) and 32
+    more V rows (per token over each 32-feature group), with the same 4-bit arithmetic as the one-shot
+    pack. The 4-bit part of the input must hold whole groups ((N - R) % 32 == 0)."""
+    blob = np.asarray(blob, dtype=np.uint8)
+    N, d, R, grp = (int(x) for x in blob[:16].view("<i4"))
+    n = N - R
+    if n % grp:
+        raise ValueError("the 4-bit part must hold whole 32-token groups to take more")
+    G = n // grp
+    nfg = -(-d // grp)
+    off = 16
+    sizes = [G * grp * d // 2, G * d * 4, n * d // 2, n * nfg * 4, R * d * 4, R * d * 4]
+    parts = []
+    for sz in sizes:
+        parts.append(blob[off:off + sz])
+        off += sz
+    kc, km, vc, vm, kr, vr = parts
+    res_k = np.concatenate([kr.view("<f4").reshape(R, d), np.asarray(k_new, dtype=np.float32).reshape(-1, d)])
+    res_v = np.concatenate([vr.view("<f4").reshape(R, d), np.asarray(v_new, dtype=np.float32).reshape(-1, d)])
+    t = res_k.shape[0] - R
+    r_out = rolled_window(R, t, r_window)
+    moved = res_k.shape[0] - r_out  # a multiple of 32
+    new_kc, new_km, new_vc, new_vm = [kc], [km], [vc], [vm]
+    for g0 in range(0, moved, grp):
+        blk = res_k[g0:g0 + grp]
+        c, s_h, m_h = _int4_codes(blk, blk.min(axis=0)[None, :], blk.max(axis=0)[None, :])
+        new_kc.append(_pack_nibbles(c).reshape(-1))
+        meta = np.stack([s_h[0], m_h[0]], axis=1).astype("<f2")  # [d, 2]
+        new_km.append(meta.view(np.uint8).reshape(-1))
+    for tok in range(moved):
+        codes = np.zeros(d, dtype=np.uint8)
+        meta = np.zeros((nfg, 2), dtype=np.float16)
+        for f in range(nfg):
+            x = res_v[tok, f * grp:(f + 1) * grp]
+            c, s_h, m_h = _int4_codes(x, x.min(), x.max())
+            codes[f * grp:(f + 1) * grp] = c
+            meta[f] = (s_h, m_h)
+        new_vc.append(_pack_nibbles(codes))
+        new_vm.append(meta.astype("<f2").view(np.uint8).reshape(-1))
+    head = np.array([N + t, d, r_out, grp], dtype="<i4").view(np.uint8)
+    out = np.concatenate([head] + new_kc + new_km + new_vc + new_vm
+                         + [res_k[moved:].astype("<f4").view(np.uint8).reshape(-1),
+                            res_v[moved:].astype("<f4").view(np.uint8).reshape(-1)])
+    assert out.size == int4kv_bytes(N + t, d, r_out)
+    return out
+
+
 def attend(q, k, v, *, scale, causal=True, q_pos0=0, region_bounds=None):
     """O = softmax(scale q k^T, causal) V for one query head, with top-32 and region masses
     (P2: attention over the whole context with the dequantized cache; the recent-window mass of the
