@@ -62,7 +62,7 @@ extern "C" {
 #define KVPROF_MODE_INT4KV 2 /* bf16 Q against packed 4-bit K/V blobs (from kvprof_pack_int4kv)     */
 
 /* Limits of this build. */
-#define KVPROF_HEAD_DIM 128      /* row_stats / attend head dimension                               */
+#define KVPROF_HEAD_DIM 128      /* head dimension of the full statistics (32 and 64: see attend)    */
 #define KVPROF_MAX_KEYS 6272     /* keys per row held on chip by one workgroup (8 waves x 49 tiles)  */
 #define KVPROF_MAX_KEYS_MX 6400  /* keys per row in MXFP8 mode (8 waves x 50 tiles)                    */
 #define KVPROF_MAX_REGIONS 8
@@ -122,6 +122,29 @@ int kvprof_pack_int4kv(const uint16_t* k, const uint16_t* v, int32_t n_heads_kv,
  * after. k_out, v_out: float32 [n_heads_kv][n_tokens][d]. Errors as for kvprof_pack_int4kv. */
 int kvprof_unpack_int4kv(const void* packed, int32_t n_heads_kv, int64_t n_tokens, int32_t d,
                          int32_t r_window, float* k_out, float* v_out, void* stream);
+
+/* Rolling float32 window ("KV residual window", section on the study's limits: it builds the cache once
+ * and names KIVI's residual mechanism — moving the oldest window tokens into the 4-bit part as tokens
+ * arrive — as what it leaves out). Window length after appending n_new tokens to a window of r_in with
+ * nominal length r_window: r = r_in + n_new if r < r_window + 32, else r - 32 * floor((r - r_window)/32)
+ * (the window keeps at least the last r_window tokens and, once full, between r_window and
+ * r_window + 31). Returns -1 for negative arguments. Host only. */
+int64_t kvprof_int4kv_append_window(int64_t r_in, int64_t n_new, int32_t r_window);
+
+/* Append n_new tokens to packed blobs with the rolling window above: the new tokens join the float32
+ * window, whose oldest tokens then move to the 4-bit part in whole 32-token groups (K per channel over
+ * the 32 tokens, V per token over 32-feature groups, the arithmetic of kvprof_pack_int4kv). The result
+ * equals, byte for byte, kvprof_pack_int4kv of all n_tokens + n_new tokens with the new window length.
+ *   packed   n_heads_kv input blobs (n_tokens tokens, window r_in), whose 4-bit part must hold whole
+ *            groups: (n_tokens - r_in) % 32 == 0. Not modified.
+ *   k_new, v_new  bf16 [n_heads_kv][n_new][d] (may be NULL when n_new == 0).
+ *   out      n_heads_kv blobs of kvprof_int4kv_bytes(n_tokens + n_new, d, new window), 4-byte aligned,
+ *            not overlapping packed.
+ * Errors: EINVAL (null pointers, negative sizes, r_in > n_tokens, partial 4-bit group, overlap,
+ * n_tokens + n_new above 2^31 - 1), ESHAPE (d not a positive multiple of 32), ESIZE (out_bytes), EALIGN. */
+int kvprof_int4kv_append(const void* packed, int32_t n_heads_kv, int64_t n_tokens, int32_t d, int32_t r_in,
+                         const uint16_t* k_new, const uint16_t* v_new, int64_t n_new, int32_t r_window,
+                         void* out, size_t out_bytes, void* stream);
 
 /* Arguments of kvprof_row_stats and kvprof_attend. Rows are (batch, query head, query) in that
  * order: row = (b * n_heads_q + h) * n_q + i; query head h reads KV head h / (n_heads_q/n_heads_kv). */
@@ -218,7 +241,10 @@ int kvprof_row_stats(const kvprof_args* a, void* stream);
  *  MiniCPM5-2B predictor study, section 0: the GQA decode shape and recall@32.)
  * Attention output O = softmax(scale q k^T + bias, causal) V over bf16 K/V (mode BF16) or over packed
  * 4-bit K/V with the float32 recent window (mode INT4KV), with any of the row statistics (the top-32
- * indices and region masses give recall@32 and the recent-window mass). o is required. */
+ * indices and region masses give recall@32 and the recent-window mass). o is required.
+ * Head dimension 128 gives every statistic. Head dimensions 32 and 64 (the residual-window study runs at
+ * 32) give o, row_max, row_lse, region_mass, support and the histograms (modes BF16 and INT4KV, any
+ * n_k < 65536); other outputs return EUNSUPPORTED. kvprof_row_stats accepts the same short heads. */
 int kvprof_attend(const kvprof_args* a, void* stream);
 
 /* Colour-range clip of a heatmap ("Catnip Week 10 KV Cache Attention Study", Figure 10: maps clipped at

@@ -96,11 +96,15 @@ def load(path: str = LIB_PATH):
     lib.kvprof_compare.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]
     lib.kvprof_ablation_bias.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
     lib.kvprof_cosine.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]
+    lib.kvprof_int4kv_append_window.restype = ctypes.c_int64
+    lib.kvprof_int4kv_append_window.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+    lib.kvprof_int4kv_append.argtypes = [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                         ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_size_t, _P]
     lib.kvprof_percentile_clip.argtypes = [_P, ctypes.c_int64, ctypes.c_double, ctypes.c_int64, _P, _P, _P]
     for name in ("kvprof_pack_mxfp8", "kvprof_unpack_mxfp8", "kvprof_pack_int4kv",
                  "kvprof_unpack_int4kv", "kvprof_row_stats", "kvprof_attend", "kvprof_row_stats_noalloc",
                  "kvprof_compare",
-                 "kvprof_ablation_bias", "kvprof_cosine", "kvprof_percentile_clip"):
+                 "kvprof_ablation_bias", "kvprof_cosine", "kvprof_percentile_clip", "kvprof_int4kv_append"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -183,6 +187,25 @@ def kvprof_pack_int4kv(k, v, r_window: int, stream=None):
     return out
 
 
+def kvprof_int4kv_append_window(r_in: int, n_new: int, r_window: int) -> int:
+    return int(load().kvprof_int4kv_append_window(r_in, n_new, r_window))
+
+
+def kvprof_int4kv_append(packed, n_tokens: int, d: int, r_in: int, k_new, v_new, r_window: int, stream=None):
+    """Append bf16 tokens k_new, v_new [heads, t, d] to packed blobs uint8 [heads, bytes] (rolling float32
+    window of nominal length r_window). Returns (new blobs uint8 [heads, bytes'], new window length)."""
+    import torch
+
+    heads, t = k_new.shape[0], k_new.shape[1]
+    r_out = kvprof_int4kv_append_window(r_in, t, r_window)
+    blob = kvprof_int4kv_bytes(n_tokens + t, d, r_out)
+    out = torch.empty((heads, blob), dtype=torch.uint8, device=packed.device)
+    _check("kvprof_int4kv_append", load().kvprof_int4kv_append(_ptr(packed), heads, n_tokens, d, r_in, _ptr(k_new),
+                                                               _ptr(v_new), t, r_window, _ptr(out), out.numel(),
+                                                               _stream(stream)))
+    return out, r_out
+
+
 def kvprof_unpack_int4kv(packed, n_tokens: int, d: int, r_window: int, stream=None):
     import torch
 
@@ -200,12 +223,12 @@ ROW_OUTPUTS = ("support", "top_mass", "top32", "strict_zero", "region_mass", "fr
                "row_lse", "o", "tv_qk", "argmax", "argmax_ref", "p_zero_frac", "tv_p", "p_rowsum")
 
 
-def _alloc_outputs(want: Sequence[str], rows: int, n_regions: int, n_frames: int, device):
+def _alloc_outputs(want: Sequence[str], rows: int, n_regions: int, n_frames: int, device, d: int = HEAD_DIM):
     import torch
 
     shapes = {"support": (rows,), "top_mass": (rows, 3), "top32": (rows, 32), "strict_zero": (rows,),
               "region_mass": (rows, n_regions), "frame_mass": (rows, n_frames), "row_max": (rows,),
-              "row_lse": (rows,), "o": (rows, HEAD_DIM), "tv_qk": (rows,), "argmax": (rows,),
+              "row_lse": (rows,), "o": (rows, d), "tv_qk": (rows,), "argmax": (rows,),
               "argmax_ref": (rows,), "p_zero_frac": (rows,), "tv_p": (rows,), "p_rowsum": (rows,)}
     ints = {"top32", "strict_zero", "argmax", "argmax_ref"}
     return {n: torch.empty(shapes[n], dtype=torch.int32 if n in ints else torch.float32, device=device)
@@ -334,7 +357,7 @@ def run(q, k=None, v=None, *, want=("support", "top_mass", "top32", "strict_zero
     rb = kw.get("region_bounds")
     n_regions = 0 if rb is None else len(rb) - 1
     n_frames = kw.get("n_frames", 0)
-    outs = _alloc_outputs(want, rows, n_regions, n_frames, q.device)
+    outs = _alloc_outputs(want, rows, n_regions, n_frames, q.device, q.shape[-1])
     hm = hm_mean = hs = None
     if heatmap:
         ng = kw["n_groups"]

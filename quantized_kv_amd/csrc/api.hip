@@ -121,13 +121,21 @@ int validate_args(const kvprof_args* a, bool need_o) {
     return fail(KVPROF_EINVAL, "unknown mode %d", a->mode);
   if (a->n_batch < 0 || a->n_heads_q < 0 || a->n_heads_kv < 0 || a->n_q < 0 || a->n_k < 0)
     return fail(KVPROF_EINVAL, "negative dimension");
-  if (a->d != KVPROF_HEAD_DIM) return fail(KVPROF_ESHAPE, "head dimension must be %d (got %d)", KVPROF_HEAD_DIM, a->d);
+  const bool short_head = a->d == 32 || a->d == 64;
+  if (a->d != KVPROF_HEAD_DIM && !short_head)
+    return fail(KVPROF_ESHAPE, "head dimension must be 32, 64 or %d (got %d)", KVPROF_HEAD_DIM, a->d);
+  if (short_head) {
+    if (a->mode == KVPROF_MODE_MXFP8) return fail(KVPROF_EUNSUPPORTED, "MXFP8 mode needs head dimension %d", KVPROF_HEAD_DIM);
+    if (a->top_mass || a->top32 || a->strict_zero || a->frame_mass || a->heatmap || a->heatmap_mean || wants_maps(a))
+      return fail(KVPROF_EUNSUPPORTED,
+                  "head dimension %d computes o, row_max, row_lse, region_mass, support and histograms only", a->d);
+  }
   if (a->n_heads_kv == 0 && a->n_heads_q != 0) return fail(KVPROF_ESHAPE, "n_heads_kv is 0");
   if (a->n_heads_kv > 0 && a->n_heads_q % a->n_heads_kv != 0)
     return fail(KVPROF_ESHAPE, "n_heads_q (%d) must be a multiple of n_heads_kv (%d)", a->n_heads_q, a->n_heads_kv);
   if (a->n_k < 1) return fail(KVPROF_ESHAPE, "n_k must be >= 1");
   if (a->n_k >= 65536) return fail(KVPROF_EUNSUPPORTED, "n_k must be < 65536");
-  const int maxk = a->mode == KVPROF_MODE_MXFP8 ? KVPROF_MAX_KEYS_MX : KVPROF_MAX_KEYS;
+  const int maxk = short_head ? 65535 : (a->mode == KVPROF_MODE_MXFP8 ? KVPROF_MAX_KEYS_MX : KVPROF_MAX_KEYS);
   if (a->n_k > maxk) return fail(KVPROF_EUNSUPPORTED, "n_k = %d exceeds the %d keys a row can hold in this mode", a->n_k, maxk);
   if (!std::isfinite(a->scale)) return fail(KVPROF_EINVAL, "scale must be finite");
   if (a->causal != 0 && a->causal != 1) return fail(KVPROF_EINVAL, "causal must be 0 or 1");
@@ -239,11 +247,64 @@ int build_segments(const kvprof_args* a, kvp::RowStatsParams& p, int tpw) {
   return KVPROF_OK;
 }
 
+// Short heads (d = 32, 64): the two-pass attention kernel, then the histograms.
+int run_short(const kvprof_args* a, hipStream_t s) {
+  const int64_t rows = total_rows(a);
+  const Workspace ws = workspace_layout(a);
+  char* wsb = reinterpret_cast<char*>(a->workspace);
+  kvp::ShortParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.n_batch = a->n_batch;
+  p.n_heads_q = a->n_heads_q;
+  p.n_heads_kv = a->n_heads_kv;
+  p.n_q = a->n_q;
+  p.n_k = a->n_k;
+  p.group = a->n_heads_kv > 0 ? a->n_heads_q / a->n_heads_kv : 0;
+  p.rows_per_kv = p.group * a->n_q;
+  p.causal = a->causal;
+  p.q_pos0 = a->q_pos0;
+  p.scale_log2 = a->scale * 1.44269504088896340736f;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.key_bias = a->key_bias;
+  p.n_regions = a->n_regions;
+  for (int i = 0; i <= a->n_regions && a->n_regions > 0; ++i) p.region_bounds[i] = a->region_bounds[i];
+  p.o = a->o;
+  p.row_max = a->row_max;
+  p.row_lse = a->row_lse;
+  p.region_mass = a->region_mass;
+  p.support = a->support;
+  if (a->hist) {
+    if (!a->support) p.support = reinterpret_cast<float*>(wsb + ws.support);
+    if (!a->region_mass && a->n_regions > 0) p.region_mass = reinterpret_cast<float*>(wsb + ws.region);
+  }
+  int ksrc = kvp::KSRC_BF16;
+  if (a->mode == KVPROF_MODE_INT4KV) {
+    ksrc = kvp::KSRC_INT4;
+    p.kv_packed = reinterpret_cast<const uint8_t*>(a->kv_packed);
+    p.blob_bytes = kvprof_int4kv_bytes(a->n_k, a->d, a->r_window);
+    p.r_window = a->r_window;
+    p.k = nullptr;
+    p.v = nullptr;
+  }
+  hipError_t e = hipSuccess;
+  if (rows > 0) e = kvp::launch_attend_short(p, a->d, ksrc, s);
+  if (e != hipSuccess) return launched(e, "short-head attention");
+  if (a->hist) {
+    e = kvp::launch_hist(p.support, p.region_mass, a->n_batch, rows > 0 ? a->n_heads_q * a->n_q : 0, a->n_regions,
+                         a->hist_bins, a->hist, s);
+    if (e != hipSuccess) return launched(e, "histogram");
+  }
+  return ok();
+}
+
 int run_rows(const kvprof_args* a, void* stream, bool need_o) {
   int st = validate_args(a, need_o);
   if (st != KVPROF_OK) return st;
   const int64_t rows = total_rows(a);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (a->d != KVPROF_HEAD_DIM) return run_short(a, s);
   const bool mx = a->mode == KVPROF_MODE_MXFP8;
   const int tpw = kvp::row_stats_tpw_for(a->n_k, mx);
   if (tpw < 0) return fail(KVPROF_EUNSUPPORTED, "n_k = %d is not supported", a->n_k);
@@ -464,6 +525,41 @@ int kvprof_unpack_int4kv(const void* packed, int32_t n_heads_kv, int64_t n_token
   return launched(kvp::launch_unpack_int4kv(reinterpret_cast<const uint8_t*>(packed), n_heads_kv, n_tokens, d,
                                             r_window, blob, k_out, v_out, reinterpret_cast<hipStream_t>(stream)),
                   "unpack_int4kv");
+}
+
+int64_t kvprof_int4kv_append_window(int64_t r_in, int64_t n_new, int32_t r_window) {
+  if (r_in < 0 || n_new < 0 || r_window < 0) return -1;
+  const int64_t r = r_in + n_new;
+  if (r < (int64_t)r_window + 32) return r;
+  return r - 32 * ((r - r_window) / 32);
+}
+
+int kvprof_int4kv_append(const void* packed, int32_t n_heads_kv, int64_t n_tokens, int32_t d, int32_t r_in,
+                         const uint16_t* k_new, const uint16_t* v_new, int64_t n_new, int32_t r_window, void* out,
+                         size_t out_bytes, void* stream) {
+  int st = check_int4(packed, out, n_heads_kv, n_tokens, d, r_in);
+  if (st != KVPROF_OK) return st;
+  if (n_new < 0 || r_window < 0) return fail(KVPROF_EINVAL, "n_new and r_window must be >= 0");
+  if ((n_tokens - r_in) % 32 != 0)
+    return fail(KVPROF_EINVAL, "the 4-bit part (%lld tokens) must hold whole 32-token groups", (long long)(n_tokens - r_in));
+  if (n_tokens + n_new > 0x7fffffffLL) return fail(KVPROF_EINVAL, "n_tokens + n_new exceeds 2^31 - 1");
+  if (n_heads_kv > 0 && n_new > 0 && (!k_new || !v_new)) return fail(KVPROF_EINVAL, "k_new / v_new is null");
+  const int64_t r_out = kvprof_int4kv_append_window(r_in, n_new, r_window);
+  const size_t bin = kvprof_int4kv_bytes(n_tokens, d, r_in);
+  const size_t bout = kvprof_int4kv_bytes(n_tokens + n_new, d, (int32_t)r_out);
+  if (out_bytes < bout * (size_t)n_heads_kv)
+    return fail(KVPROF_ESIZE, "out needs %zu bytes (got %zu)", bout * (size_t)n_heads_kv, out_bytes);
+  if ((packed && !aligned(packed, 4)) || (out && !aligned(out, 4))) return fail(KVPROF_EALIGN, "blobs must be 4-byte aligned");
+  if ((k_new && !aligned(k_new, 2)) || (v_new && !aligned(v_new, 2))) return fail(KVPROF_EALIGN, "k_new / v_new must be 2-byte aligned");
+  if (n_heads_kv > 0) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(packed), a1 = a0 + bin * (size_t)n_heads_kv;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(out), b1 = b0 + bout * (size_t)n_heads_kv;
+    if (a0 < b1 && b0 < a1) return fail(KVPROF_EINVAL, "out overlaps packed");
+  }
+  return launched(kvp::launch_int4kv_append(reinterpret_cast<const uint8_t*>(packed), n_heads_kv, n_tokens, d, r_in,
+                                            k_new, v_new, n_new, (int)r_out, reinterpret_cast<uint8_t*>(out), bin,
+                                            bout, reinterpret_cast<hipStream_t>(stream)),
+                  "int4kv_append");
 }
 
 size_t kvprof_workspace_bytes(const kvprof_args* a) {

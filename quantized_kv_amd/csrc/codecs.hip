@@ -368,6 +368,167 @@ hipError_t launch_unpack_mxfp8(const uint8_t* codes, const uint8_t* scales, int6
   return hipGetLastError();
 }
 
+// ---- rolling window: append tokens, move the oldest float32 tokens to the 4-bit part ----------------
+// The combined window of a head is its old float32 tokens followed by the new bf16 tokens; token u of it
+// reads the old window for u < R_in and the new tokens after (bf16 -> fp32 is exact, so a moved token
+// is quantized from the same value the one-shot pack would see).
+struct AppendGeom {
+  Int4Layout Lo, Ln;  // old and new blob layouts
+  int d, r_in;
+  int64_t t;          // new tokens per head
+  int64_t moved;      // tokens moved to the 4-bit part (a multiple of 32)
+  size_t blob_in, blob_out;
+};
+
+__device__ __forceinline__ float win_val(const uint8_t* ib, const uint16_t* xnew, const AppendGeom& g, size_t res_off,
+                                         int h, int64_t u, int c) {
+  if (u < g.r_in) return reinterpret_cast<const float*>(ib + res_off)[u * g.d + c];
+  return bf16_to_f32(xnew[((int64_t)h * g.t + (u - g.r_in)) * g.d + c]);
+}
+
+// The old 4-bit sections, copied a word at a time to their new offsets.
+__global__ void append_copy_kernel(const uint8_t* __restrict__ in, uint8_t* __restrict__ out, int heads, AppendGeom g) {
+  const int64_t wkc = (g.Lo.km - g.Lo.kc) / 4, wkm = (g.Lo.vc - g.Lo.km) / 4, wvc = (g.Lo.vm - g.Lo.vc) / 4,
+                wvm = (g.Lo.kr - g.Lo.vm) / 4;
+  const int64_t per = wkc + wkm + wvc + wvm;
+  const int64_t total = (int64_t)heads * per;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int h = (int)(t / per);
+    int64_t e = t - (int64_t)h * per;
+    size_t so, dst;
+    if (e < wkc) {
+      so = g.Lo.kc;
+      dst = g.Ln.kc;
+    } else if ((e -= wkc) < wkm) {
+      so = g.Lo.km;
+      dst = g.Ln.km;
+    } else if ((e -= wkm) < wvc) {
+      so = g.Lo.vc;
+      dst = g.Ln.vc;
+    } else {
+      e -= wvc;
+      so = g.Lo.vm;
+      dst = g.Ln.vm;
+    }
+    const uint32_t w = reinterpret_cast<const uint32_t*>(in + (size_t)h * g.blob_in + so)[e];
+    reinterpret_cast<uint32_t*>(out + (size_t)h * g.blob_out + dst)[e] = w;
+  }
+}
+
+// New K groups: one thread per (head, moved group, channel pair), as pack_k_kernel.
+__global__ void append_k_kernel(const uint8_t* __restrict__ in, const uint16_t* __restrict__ knew, uint8_t* __restrict__ out,
+                                int heads, AppendGeom g) {
+  const int64_t ng = g.moved / 32, G0 = g.Lo.G;
+  const int d = g.d;
+  const int64_t total = (int64_t)heads * ng * (d / 2);
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int cp = (int)(t % (d / 2));
+    const int64_t gi = (t / (d / 2)) % ng;
+    const int h = (int)(t / ((d / 2) * ng));
+    const uint8_t* ib = in + (size_t)h * g.blob_in;
+    uint8_t* ob = out + (size_t)h * g.blob_out;
+    Int4Meta mt[2];
+    for (int q = 0; q < 2; ++q) {
+      const int c = 2 * cp + q;
+      float lo = INFINITY, hi = -INFINITY;
+      for (int64_t u = gi * 32; u < gi * 32 + 32; ++u) {
+        const float xv = win_val(ib, knew, g, g.Lo.kr, h, u, c);
+        lo = fminf(lo, xv);
+        hi = fmaxf(hi, xv);
+      }
+      mt[q] = int4_meta(lo, hi);
+      _Float16* meta = reinterpret_cast<_Float16*>(ob + g.Ln.km) + ((G0 + gi) * d + c) * 2;
+      meta[0] = mt[q].s;
+      meta[1] = mt[q].m;
+    }
+    for (int64_t u = gi * 32; u < gi * 32 + 32; ++u) {
+      const uint32_t byte = int4_code(win_val(ib, knew, g, g.Lo.kr, h, u, 2 * cp), mt[0]) |
+                            (int4_code(win_val(ib, knew, g, g.Lo.kr, h, u, 2 * cp + 1), mt[1]) << 4);
+      ob[g.Ln.kc + (G0 * 32 + u) * (d / 2) + cp] = (uint8_t)byte;
+    }
+  }
+}
+
+// New V rows: one thread per (head, moved token, 32-feature group), as pack_v_kernel.
+__global__ void append_v_kernel(const uint8_t* __restrict__ in, const uint16_t* __restrict__ vnew, uint8_t* __restrict__ out,
+                                int heads, AppendGeom g) {
+  const int d = g.d, nfg = d / 32;
+  const int64_t n0 = g.Lo.n;
+  const int64_t total = (int64_t)heads * g.moved * nfg;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int f = (int)(t % nfg);
+    const int64_t u = (t / nfg) % g.moved;
+    const int h = (int)(t / (nfg * g.moved));
+    const uint8_t* ib = in + (size_t)h * g.blob_in;
+    uint8_t* ob = out + (size_t)h * g.blob_out;
+    float lo = INFINITY, hi = -INFINITY;
+    for (int c = 0; c < 32; ++c) {
+      const float xv = win_val(ib, vnew, g, g.Lo.vr, h, u, f * 32 + c);
+      lo = fminf(lo, xv);
+      hi = fmaxf(hi, xv);
+    }
+    const Int4Meta mt = int4_meta(lo, hi);
+    _Float16* meta = reinterpret_cast<_Float16*>(ob + g.Ln.vm) + ((n0 + u) * nfg + f) * 2;
+    meta[0] = mt.s;
+    meta[1] = mt.m;
+    for (int c = 0; c < 32; c += 2) {
+      const uint32_t byte = int4_code(win_val(ib, vnew, g, g.Lo.vr, h, u, f * 32 + c), mt) |
+                            (int4_code(win_val(ib, vnew, g, g.Lo.vr, h, u, f * 32 + c + 1), mt) << 4);
+      ob[g.Ln.vc + (n0 + u) * (d / 2) + (f * 32 + c) / 2] = (uint8_t)byte;
+    }
+  }
+}
+
+// Header and the new float32 window (the combined window's tokens from `moved` on).
+__global__ void append_tail_kernel(const uint8_t* __restrict__ in, const uint16_t* __restrict__ knew,
+                                   const uint16_t* __restrict__ vnew, uint8_t* __restrict__ out, int heads, AppendGeom g) {
+  const int64_t rn = g.r_in + g.t - g.moved;
+  const int64_t per = rn * g.d;
+  const int64_t total = (int64_t)heads * (per + 1);
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int h = (int)(t / (per + 1));
+    const int64_t e = t % (per + 1);
+    const uint8_t* ib = in + (size_t)h * g.blob_in;
+    uint8_t* ob = out + (size_t)h * g.blob_out;
+    if (e == per) {
+      int32_t* hd = reinterpret_cast<int32_t*>(ob);
+      hd[0] = (int32_t)(g.Lo.n + g.r_in + g.t);
+      hd[1] = g.d;
+      hd[2] = (int32_t)rn;
+      hd[3] = 32;
+      continue;
+    }
+    const int64_t u = g.moved + e / g.d;
+    const int c = (int)(e % g.d);
+    reinterpret_cast<float*>(ob + g.Ln.kr)[e] = win_val(ib, knew, g, g.Lo.kr, h, u, c);
+    reinterpret_cast<float*>(ob + g.Ln.vr)[e] = win_val(ib, vnew, g, g.Lo.vr, h, u, c);
+  }
+}
+
+hipError_t launch_int4kv_append(const uint8_t* in, int heads, int64_t N, int d, int r_in, const uint16_t* knew,
+                                const uint16_t* vnew, int64_t t, int r_out, uint8_t* out, size_t blob_in,
+                                size_t blob_out, hipStream_t s) {
+  if (heads == 0) return hipSuccess;
+  AppendGeom g;
+  g.Lo = int4_layout(N, d, r_in);
+  g.Ln = int4_layout(N + t, d, r_out);
+  g.d = d;
+  g.r_in = r_in;
+  g.t = t;
+  g.moved = (int64_t)r_in + t - r_out;
+  g.blob_in = blob_in;
+  g.blob_out = blob_out;
+  const int64_t ncopy = (int64_t)heads * (int64_t)((g.Lo.kr - g.Lo.kc) / 4);
+  const int64_t nk = (int64_t)heads * (g.moved / 32) * (d / 2);
+  const int64_t nv = (int64_t)heads * g.moved * (d / 32);
+  const int64_t nt = (int64_t)heads * ((int64_t)r_out * d + 1);
+  if (ncopy > 0) hipLaunchKernelGGL(append_copy_kernel, dim3(grid_for(ncopy, 256)), dim3(256), 0, s, in, out, heads, g);
+  if (nk > 0) hipLaunchKernelGGL(append_k_kernel, dim3(grid_for(nk, 128)), dim3(128), 0, s, in, knew, out, heads, g);
+  if (nv > 0) hipLaunchKernelGGL(append_v_kernel, dim3(grid_for(nv, 128)), dim3(128), 0, s, in, vnew, out, heads, g);
+  hipLaunchKernelGGL(append_tail_kernel, dim3(grid_for(nt, 256)), dim3(256), 0, s, in, knew, vnew, out, heads, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_int4kv(const uint16_t* k, const uint16_t* v, int heads, int64_t N, int d,
                               int R, uint8_t* out, size_t blob, hipStream_t s) {
   if (heads == 0) return hipSuccess;

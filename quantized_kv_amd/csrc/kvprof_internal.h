@@ -16,6 +16,9 @@ hipError_t launch_unpack_mxfp8(const uint8_t* codes, const uint8_t* scales, int6
                                float* out_f32, uint16_t* out_bf16, hipStream_t s);
 hipError_t launch_pack_int4kv(const uint16_t* k, const uint16_t* v, int heads, int64_t N, int d,
                               int R, uint8_t* out, size_t blob_bytes, hipStream_t s);
+hipError_t launch_int4kv_append(const uint8_t* in, int heads, int64_t N, int d, int r_in, const uint16_t* knew,
+                                const uint16_t* vnew, int64_t t, int r_out, uint8_t* out, size_t blob_in,
+                                size_t blob_out, hipStream_t s);
 hipError_t launch_unpack_int4kv(const uint8_t* packed, int heads, int64_t N, int d, int R,
                                 size_t blob_bytes, float* k_out, float* v_out, hipStream_t s);
 
@@ -92,6 +95,28 @@ hipError_t launch_hist(const float* support, const float* region_mass, int n_bat
 hipError_t launch_compare(const float* oq, const float* oref, const int* tq, const int* tref,
                           int64_t rows, int d, float* rel_row, float* recall_row, double* sums,
                           hipStream_t s);
+
+// ---- short heads (attend_short.hip) ----------------------------------------------------------------
+
+struct ShortParams {
+  int n_batch, n_heads_q, n_heads_kv, n_q, n_k;
+  int group, rows_per_kv, causal;
+  long long q_pos0;
+  float scale_log2;
+  const uint16_t* q;  // bf16 [b][hq][nq][d]
+  const uint16_t* k;  // bf16 [b][hkv][nk][d]
+  const uint16_t* v;
+  const uint8_t* kv_packed;  // INT4 mode: one blob per (b, hkv)
+  size_t blob_bytes;
+  int r_window;
+  const float* key_bias;
+  int n_regions;
+  int region_bounds[KVPROF_MAX_REGIONS + 1];
+  float *o, *row_max, *row_lse, *region_mass, *support;
+};
+
+// d = 32 or 64; ksrc = KSRC_BF16 or KSRC_INT4.
+hipError_t launch_attend_short(const ShortParams& p, int d, int ksrc, hipStream_t s);
 
 // ---- probability maps (maps.hip) -------------------------------------------------------------------
 

@@ -149,6 +149,34 @@ def tiny_inputs(seed: int = 1):
     return Q, K, V
 
 
+P2_SEEDS = (1, 2, 3)
+P2_LENGTHS = (128, 512)
+P2_D = 32
+P2_WINDOWS = (0, 16, 64)
+P2_FOCUS = 4.85  # recent_focus then puts about 77 % of the reference mass on the last 16 tokens
+P2_FOCUS_TOKENS = 16
+
+
+def p2_inputs(seed: int, n: int, variant: str, d: int = P2_D):
+    """One input of the fixed-budget residual-window protocol: Q, K, V = standard_normal((n, d), float32)
+    drawn in that order from default_rng(seed). early_focus adds P2_FOCUS to channel 0 of every query and
+    of the first 16 keys, recent_focus to channel 0 of every query and of the last 16 keys; both start
+    from the same base arrays as clean. Returns bf16 tensors [n, d]."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((n, d), dtype=np.float32)
+    k = rng.standard_normal((n, d), dtype=np.float32)
+    v = rng.standard_normal((n, d), dtype=np.float32)
+    if variant == "early_focus":
+        q[:, 0] += P2_FOCUS
+        k[:P2_FOCUS_TOKENS, 0] += P2_FOCUS
+    elif variant == "recent_focus":
+        q[:, 0] += P2_FOCUS
+        k[n - P2_FOCUS_TOKENS:, 0] += P2_FOCUS
+    elif variant != "clean":
+        raise ValueError(variant)
+    return to_bf16(q), to_bf16(k), to_bf16(v)
+
+
 def hadamard_signs(seed: int = 4, n: int = HEAD_DIM) -> np.ndarray:
     """Random signs for the signed Hadamard rotation: 2*default_rng(seed).integers(0,2,n)-1 (int8)."""
     return (2 * np.random.default_rng(seed).integers(0, 2, n) - 1).astype(np.int8)

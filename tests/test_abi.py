@@ -74,7 +74,9 @@ def _args(**over):
 
 
 @pytest.mark.parametrize("over,code,needle", [
-    (dict(d=64), B.KVPROF_ESHAPE, "head dimension"),
+    (dict(d=48), B.KVPROF_ESHAPE, "head dimension"),
+    (dict(d=64, top32=0x30000), B.KVPROF_EUNSUPPORTED, "head dimension 64"),
+    (dict(d=32, mode=B.MODE_MXFP8, q_codes=1, q_scales=1, k_codes=1, k_scales=1), B.KVPROF_EUNSUPPORTED, "MXFP8"),
     (dict(n_heads_q=3), B.KVPROF_ESHAPE, "multiple of n_heads_kv"),
     (dict(n_k=7000), B.KVPROF_EUNSUPPORTED, "exceeds"),
     (dict(n_k=0), B.KVPROF_ESHAPE, "n_k"),
@@ -188,6 +190,9 @@ _SIGNATURES = {
     "kvprof_workspace_bytes": ("size_t", ["const kvprof_args*"]),
     "kvprof_row_stats": ("int", ["const kvprof_args*", "void*"]),
     "kvprof_attend": ("int", ["const kvprof_args*", "void*"]),
+    "kvprof_int4kv_append_window": ("int64_t", ["int64_t", "int64_t", "int32_t"]),
+    "kvprof_int4kv_append": ("int", ["const void*", "int32_t", "int64_t", "int32_t", "int32_t", "const uint16_t*",
+                                     "const uint16_t*", "int64_t", "int32_t", "void*", "size_t", "void*"]),
     "kvprof_percentile_clip": ("int", ["const float*", "int64_t", "double", "int64_t", "float*", "float*",
                                        "void*"]),
 }
@@ -228,7 +233,7 @@ def test_noalloc_rejects_oversized_scratch_before_device_work(lib):
     assert lib.kvprof_row_stats_noalloc(ctypes.byref(a), None) == B.KVPROF_ESIZE
     assert "allocation-free" in _err(lib)
     assert lib.kvprof_row_stats_noalloc(None, None) == B.KVPROF_EINVAL
-    a = _args(d=64)
+    a = _args(d=48)
     assert lib.kvprof_row_stats_noalloc(ctypes.byref(a), None) == B.KVPROF_ESHAPE
 
 
@@ -278,3 +283,28 @@ def test_percentile_clip_validation(lib):
     assert f(fake, 10, 99.5, 0, fake, None, None) == B.KVPROF_EINVAL
     assert f(None, 10, 99.5, 8, fake, None, None) == B.KVPROF_EINVAL
     assert f(ctypes.c_void_p(0x10002), 10, 99.5, 8, fake, None, None) == B.KVPROF_EALIGN
+
+
+def test_append_window_rule_matches_oracle(lib):
+    from oracle import kvprof_oracle as O
+
+    for r_in in range(0, 90, 5):
+        for t in range(0, 130, 7):
+            for R in (0, 16, 64):
+                assert B.kvprof_int4kv_append_window(r_in, t, R) == O.rolled_window(r_in, t, R)
+    assert B.kvprof_int4kv_append_window(-1, 0, 0) == -1
+
+
+def test_append_validation(lib):
+    fake = ctypes.c_void_p(0x10000)
+    f = lib.kvprof_int4kv_append
+    big = 1 << 30
+    # 112 tokens in the 4-bit part: not whole groups
+    assert f(fake, 2, 128, 32, 16, fake, fake, 1, 16, ctypes.c_void_p(0x10000000), big, None) == B.KVPROF_EINVAL
+    assert "whole" in _err(lib)
+    assert f(fake, 2, 128, 48, 0, fake, fake, 1, 16, ctypes.c_void_p(0x10000000), big, None) == B.KVPROF_ESHAPE
+    assert f(fake, 2, 128, 32, 0, None, fake, 1, 16, ctypes.c_void_p(0x10000000), big, None) == B.KVPROF_EINVAL
+    assert f(fake, 2, 128, 32, 0, fake, fake, 1, 16, ctypes.c_void_p(0x10000000), 100, None) == B.KVPROF_ESIZE
+    assert f(fake, 2, 128, 32, 0, fake, fake, 1, 16, ctypes.c_void_p(0x10001), big, None) == B.KVPROF_EALIGN
+    assert f(fake, 2, 128, 32, 0, fake, fake, 1, 16, ctypes.c_void_p(0x10100), big, None) == B.KVPROF_EINVAL  # overlap
+    assert "overlaps" in _err(lib)
