@@ -10,7 +10,8 @@ reports, inputs already resident in HBM:
              frames x 390 tokens, [sink 4 | recent 6 | current 6] frames), +0.5 current-chunk bias;
              support, top-1/5/10 % mass, top-32 indices, strict zeros, region and frame masses,
              row max / lse, the 6x16 per-head temporal heatmaps and per-record histograms.
-* full_rows: the same for 2,340 queries per head (one record per step by default, --records).
+* full_rows: the same for all 2,340 queries per head, 42 records per step (3,144,960 rows); the
+             default run also measures it and reports it under "full_rows" (--no-full-rows skips it).
 * decode   : 16 query heads sharing 2 KV heads, 4,096 cached keys, last 256 positions, attention
              output over the packed 4-bit K/V (R = 16) with top-32 and recent-window mass.
 * decode_batch: one decode step for 512 sequences (seeds 5000 + b): each sequence's last position,
@@ -53,6 +54,7 @@ def parse():
     ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode", "decode_batch", "mx_sampled", "ablation", "tiny"])
     ap.add_argument("--records", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-full-rows", action="store_true", help="skip the full-row sub-measurement of the default run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy instead (counter calibration)")
     return ap.parse_args()
@@ -107,9 +109,9 @@ def time_it(fn, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps  # ms per call
 
 
-def cpu_baseline_video(n_records: int, sampled: bool, threads=1):
-    """The oracle, as it stands, on the first n_records records (all heads), with `threads` BLAS
-    threads (None: every core of the host)."""
+def cpu_baseline_video(n_records: int, sampled: bool, threads=1, heads=None):
+    """The oracle, as it stands, on the first n_records records (all heads, or the first `heads`), with
+    `threads` BLAS threads (None: every core of the host)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -123,7 +125,7 @@ def cpu_baseline_video(n_records: int, sampled: bool, threads=1):
         q, k = inputs.bf16_values(rec.q), inputs.bf16_values(rec.k)
         with threadpool_limits(threads):
             t = time.perf_counter()
-            for h in range(q.shape[0]):
+            for h in range(q.shape[0] if heads is None else heads):
                 O.row_stats(q[h], k[h], scale=128 ** -0.5, key_bias=bias,
                             region_bounds=inputs.VIDEO_REGION_BOUNDS, frame_len=inputs.LF_TOKENS,
                             n_frames=inputs.N_KEY_FRAMES)
@@ -136,8 +138,19 @@ def cpu_baseline_video(n_records: int, sampled: bool, threads=1):
     else:
         cores = threads
     return {"value": round(rows / dt, 1), "unit": "rows/s", "cores": cores, "kind": "oracle",
-            "sample": f"records 0..{n_records - 1}, {q.shape[0]} heads x {q.shape[1]} queries x 6240 keys "
-                      f"({rows} rows, {dt:.1f} s of oracle time)"}
+            "sample": f"records 0..{n_records - 1}, {q.shape[0] if heads is None else heads} heads x {q.shape[1]} "
+                      f"queries x 6240 keys ({rows} rows, {dt:.1f} s of oracle time)",
+            "cpu": cpu_model()}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def copy_calibration(args):
@@ -173,7 +186,7 @@ def run_video(args, sampled: bool):
     from quantized_kv_amd import inputs
 
     dev = torch.device("cuda:0")
-    n_rec = args.records or (inputs.N_RECORDS if sampled else 1)
+    n_rec = args.records or inputs.N_RECORDS
     t_gen = time.time()
     Q, K = video_inputs(n_rec, sampled, dev)
     gen_s = time.time() - t_gen
@@ -224,9 +237,12 @@ def run_video(args, sampled: bool):
         "input_gen_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_video(6 if sampled else 1, sampled)
-        # the same oracle with NumPy's BLAS on every host core (its per-row loops stay single-threaded)
-        out["cpu_baseline_all_cores"] = cpu_baseline_video(3 if sampled else 1, sampled, threads=None)
+        if sampled:
+            out["cpu_baseline"] = cpu_baseline_video(6, True)
+            # the same oracle with NumPy's BLAS on every host core (its per-row loops stay single-threaded)
+            out["cpu_baseline_all_cores"] = cpu_baseline_video(3, True, threads=None)
+        else:
+            out["cpu_baseline"] = cpu_baseline_video(1, False, heads=4)
     return out
 
 
@@ -561,6 +577,16 @@ def main():
         out = run_ablation(args)
     else:
         out = run_video(args, sampled=args.workload == "sampled")
+        if args.workload == "sampled" and not args.no_full_rows:
+            # the full-row configuration (all 2,340 queries of each head, 42 records) on the same GPU,
+            # reported beside the sampled line with its own MFMA roofline
+            torch.cuda.empty_cache()
+            print("bench: sampled done, measuring full rows", file=sys.stderr, flush=True)
+            sub = argparse.Namespace(**{**vars(args), "steps": min(args.steps, 10), "warmup": min(args.warmup, 2),
+                                        "records": None})
+            fr = run_video(sub, sampled=False)
+            out["full_rows"] = {k: fr[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "config",
+                                                   "roofline", "row_kernel_ms", "cpu_baseline") if k in fr}
     print(json.dumps(out), flush=True)
 
 

@@ -47,6 +47,7 @@ constexpr unsigned long long kOne = 1ull << 44;            // one key in a packe
 constexpr unsigned long long kMassMask = (1ull << 44) - 1;
 constexpr float kNegBig = -1.0e37f;  // floor of the staged key bias
 constexpr float kSelSigma = 0.8f;    // selection threshold: about mean + kSelSigma standard deviations
+constexpr float kInterpTol = 4e-4f;  // bound on a top-f mass taken by interpolation inside its bin
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -69,6 +70,8 @@ struct TState {
   int cnt_in;             // elements in the group
   int target;             // 0-based rank to locate
   int resolved;
+  int interp;             // top-f target whose mass comes from the level-1 bin by interpolation
+  unsigned long long mass_in;      // interp: fixed-point mass of the target's bin
   unsigned long long mass_before;  // fixed-point mass (units of 1 / Z') ranked before the group
   float frac;
 };
@@ -375,6 +378,7 @@ __device__ __forceinline__ void init_target(TState& ts, int t, int n) {
   ts.cnt_before = 0;
   ts.cnt_in = 0;
   ts.resolved = n > 0 ? 0 : 1;
+  ts.interp = 0;
   ts.mass_before = 0;
   if (t == 0) {
     ts.target = min(31, n - 1);
@@ -386,9 +390,35 @@ __device__ __forceinline__ void init_target(TState& ts, int t, int n) {
   }
 }
 
+// Top-f mass of an interpolated target (see scan_row): the mass before its bin plus the share of the
+// bin's mass taken by its first rr keys and frac of the next, with the bin's keys evenly spaced in score.
+__device__ __forceinline__ float interp_mass(const TState& ts, float k8, float z) {
+  const float wbin = k8 > 0.f ? 1.f / k8 : 0.f;  // bin width (log2 units)
+  const float cf = (float)ts.cnt_in;
+  const float rr = (float)(ts.target - ts.cnt_before);
+  float share;
+  if (wbin < 1e-3f) {  // (1 - x^k) would lose its relative precision; the bin is flat to 1e-3
+    share = (rr + ts.frac) / cf;
+  } else {
+    const float a = wbin / cf;  // x = 2^-a
+    const float xr = __builtin_amdgcn_exp2f(-rr * a);
+    const float top = (1.f - xr) + ts.frac * xr * (1.f - __builtin_amdgcn_exp2f(-a));
+    share = top / (1.f - __builtin_amdgcn_exp2f(-wbin));
+  }
+  return ((float)ts.mass_before + share * (float)ts.mass_in) / z;
+}
+
 // Per-row scan of the level-1 histogram by one wave (lane holds bins 4*lane..4*lane+3): locates, for
 // every target of the row, the bin that holds its rank. A row whose histogram holds no more keys than
 // its deepest target is marked for a redo over every visible key.
+//
+// A top-f mass (targets 1..3) is the mass before its bin plus the share of the bin's mass held by the
+// bin's first rr keys and frac of the next (rr = rank - keys before the bin). Taking the bin's c keys as
+// evenly spaced in score across the bin's width w (log2 units) gives that share in closed form,
+// [1 - x^rr + frac x^rr (1 - x)] / (1 - x^c) with x = 2^(-w/c). Whatever the keys' placement inside the
+// bin, the true share differs from it by less than about 0.35 w times the bin's mass; when that bound
+// is within kInterpTol the target takes no part in the exact rank passes (decided at the start of
+// phase D, computed by interp_mass where the outputs are written).
 template <typename SM>
 __device__ void scan_row(SM& sm, int row, int lane) {
   unsigned c[4];
@@ -846,6 +876,23 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   // each target with further radix levels.
   if (tid == 0) sm.flag = 0;
   __syncthreads();
+  // top-f targets (lanes 1..3 of the row's wave) whose bin is narrow enough take the interpolated mass
+  // (see interp_mass) and leave the exact rank passes; the test needs no division
+  for (int row = w; row < ROWS; row += NW) {
+    if (lane >= 1 && lane < NT) {
+      TState& ts = sm.ts[row][lane];
+      if (ts.valid && ts.ph == 0 && ts.prefix < 256u) {
+        const unsigned long long mb = sm.u.sel.hist[row][ts.prefix] & kMassMask;
+        const float k8 = sm.r_k8[row];
+        const float wbin = k8 > 0.f ? __builtin_amdgcn_rcpf(k8) : 0.f;
+        if ((float)mb * (0.35f * wbin) <= kInterpTol * sm.r_z[row]) {
+          ts.mass_in = mb;
+          ts.interp = 1;
+          ts.resolved = 1;
+        }
+      }
+    }
+  }
   for (int row = w; row < ROWS; row += NW) {
     // all four states read at once (one LDS round trip), then a wave-uniform test
     unsigned pv[NT];
@@ -854,7 +901,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     for (int t = 0; t < NT; ++t) {
       pv[t] = sm.ts[row][t].prefix;
       cin[t] = sm.ts[row][t].cnt_in;
-      val[t] = sm.ts[row][t].valid;
+      val[t] = sm.ts[row][t].valid && !sm.ts[row][t].interp;  // interpolated targets need no ranks
       res[t] = sm.ts[row][t].resolved;
     }
     int tot = 0, bad = 0;
@@ -890,7 +937,11 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       // 31 + CAP keys) and of the other boundary bins.
       int bq[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) bq[t] = sm.ts[r][t].valid ? (int)sm.ts[r][t].prefix : -1;
+      for (int t = 0; t < NT; ++t) bq[t] = (sm.ts[r][t].valid && !sm.ts[r][t].interp) ? (int)sm.ts[r][t].prefix : -1;
+      // When no row of the wave has an exact top-f target left, a key belongs to the list iff its
+      // level-1 bin is at most bq0: u >= T and fma(-u, k8, m k8) < bq0 + 1 (the bin before clamping
+      // and truncation), one compare pair instead of the bin and four tests.
+      const bool only32 = __ballot((bq[1] >= 0) | (bq[2] >= 0) | (bq[3] >= 0)) == 0ull;
       // Two passes without returning atomics in the loop: mark and count this lane's list keys (one
       // bit per key, 8 tiles per word, kept in LDS), reserve slots with one atomic, then write.
       static_assert((TPW + 7) / 8 <= 7, "gather bit words");
@@ -898,6 +949,25 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       {
         const float Tq = rc_T(), k8q = rc_k8(), mk8q = __fmul_rn(rc_m(), k8q);
         unsigned bits = 0u;
+        if (only32) {
+          const float lim = bq[0] < 0 ? -INFINITY : (bq[0] >= 255 ? INFINITY : (float)(bq[0] + 1));
+#pragma unroll
+          for (int tt = 0; tt < TPW; ++tt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float u = scr(tt, i);
+              const bool in = (u >= Tq) & (__fmaf_rn(-u, k8q, mk8q) < lim);
+              bits |= in ? 1u << (4 * (tt & 7) + i) : 0u;
+            }
+            if ((tt & 7) == 7 || tt == TPW - 1) {
+              sm.u.sel.gbits[tt >> 3][w][lane] = bits;
+              nc += __builtin_popcount(bits);
+              bits = 0u;
+            }
+            bits = opaque(bits);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
 #pragma unroll
@@ -914,6 +984,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           }
           bits = opaque(bits);
           __builtin_amdgcn_sched_barrier(0);
+        }
         }
       }
       int cpos = nc ? atomicAdd(&sm.ncand[r], nc) : 0;
@@ -947,7 +1018,9 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       const int c4 = (c + 3) & ~3;
       if (c + lane < c4) sm.u.sel.ck[row][c + lane] = ~0ull;
       const int b0 = sm.ts[row][0].valid ? (int)sm.ts[row][0].prefix : -1;
-      const int b1 = (int)sm.ts[row][1].prefix, b2 = (int)sm.ts[row][2].prefix, b3 = (int)sm.ts[row][3].prefix;
+      const int b1 = sm.ts[row][1].interp ? -1 : (int)sm.ts[row][1].prefix;
+      const int b2 = sm.ts[row][2].interp ? -1 : (int)sm.ts[row][2].prefix;
+      const int b3 = sm.ts[row][3].interp ? -1 : (int)sm.ts[row][3].prefix;
       for (int a0 = 0; a0 < c; a0 += 64) {
         const int a = a0 + lane;
         const unsigned long long ka = a < c ? sm.u.sel.ck[row][a] : 0ull;
@@ -986,7 +1059,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const TState& ts = sm.ts[row][t];
-          if (!ts.valid || ts.prefix != dga) continue;
+          if (!ts.valid || ts.interp || ts.prefix != dga) continue;
           const int rr = ts.target - ts.cnt_before;
           if (t == 0) {
             if (rk <= rr) {  // ranks 0..target of the top-32 list
@@ -1003,7 +1076,8 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       for (int t = 1; t < NT; ++t) {
         unsigned long long x = acc[t];
         for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-        if (lane == 0 && ri.ok) sm.tmass[row][t - 1] = (float)(sm.ts[row][t].mass_before + x) / sm.r_z[row];
+        if (lane == 0 && ri.ok && !sm.ts[row][t].interp)
+          sm.tmass[row][t - 1] = (float)(sm.ts[row][t].mass_before + x) / sm.r_z[row];
       }
     }
     __syncthreads();
@@ -1109,7 +1183,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       if (t == 0) sm.nwin[tid] = 0;
     }
     __syncthreads();
-    if (sm.ts[r][t].valid) {
+    if (sm.ts[r][t].valid && !sm.ts[r][t].interp) {
       const int ph = opaque(sm.ts[r][t].ph), sh = opaque(sm.ts[r][t].sh);
       const unsigned pre = opaque(sm.ts[r][t].prefix), dfix = opaque(sm.ts[r][t].dfix);
       const int gq = opaque(g);
@@ -1147,7 +1221,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       const TState ts = sm.ts[row][t];
       const int c = min(sm.ncand[row], CAP);
       const float mr = sm.r_m[row], k32r = sm.r_k8[row] * 0x1p24f, mk32r = __fmul_rn(mr, sm.r_k8[row]) * 0x1p24f;
-      if (ts.valid) {
+      if (ts.valid && !ts.interp) {
         for (int a = lane; a < c; a += 64) {
           const float ua = sm.u.sel.ce[row][a];
           const int ja = sm.u.sel.cj[row][a];
@@ -1174,7 +1248,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     if (t > 0) for (int row = w; row < ROWS; row += NW) {
       const TState ts = sm.ts[row][t];
       const RowInfo ri = row_info(p, b, hkv, rb, row);
-      if (ri.ok && ts.valid) {
+      if (ri.ok && ts.valid && !ts.interp) {
         const int rr = ts.target - ts.cnt_before;
         const int c = min(sm.ncand[row], CAP);
         float a = 0.f;
@@ -1222,9 +1296,13 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         const float H = logf(z) - kLn2 * (e_ / z);
         if (p.support) p.support[ri.grow] = expf(H) / (float)ri.nvis;
         if (p.top_mass) {
-          p.top_mass[ri.grow * 3 + 0] = sm.tmass[row][0];
-          p.top_mass[ri.grow * 3 + 1] = sm.tmass[row][1];
-          p.top_mass[ri.grow * 3 + 2] = sm.tmass[row][2];
+#pragma unroll 1
+          for (int t = 1; t < NT; ++t) {
+            const TState& ts = sm.ts[row][t];
+            float mass = sm.tmass[row][t - 1];
+            if (ts.interp) mass = interp_mass(ts, sm.r_k8[row], z);
+            p.top_mass[ri.grow * 3 + t - 1] = mass;
+          }
         }
       }
     }
