@@ -582,6 +582,12 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) pf4[ks] = load_k4_raw(rk, L, kbase + r, ks * 32 + 8 * g);
   }
+  // bf16 keys: this lane's Q fragments stay in registers for the score pass (read from LDS once
+  // instead of once per tile: a third of the pass's LDS traffic). The int4 path, whose prefetched raw
+  // words need those registers, keeps reading them from LDS.
+  u32x4 qfr[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qfr[ks] = KSRC == KSRC_BF16 ? sm.qs[r][ks * 4 + g] : zero4();
   // The scheduling barrier at the end of each tile keeps the compiler from hoisting every tile's
   // loads, which would push the score registers out to scratch.
 #pragma unroll
@@ -599,7 +605,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       if (j0 < kmax) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)  // chunk 4ks + g of key r (see issue)
-          acc = mfma_step<KSRC>(sm.u.a.ring[w][t % kRing][r >> 2][(r & 3) * 16 + ((4 * ks + g) ^ r)], sm.qs[r][ks * 4 + g], acc);
+          acc = mfma_step<KSRC>(sm.u.a.ring[w][t % kRing][r >> 2][(r & 3) * 16 + ((4 * ks + g) ^ r)], qfr[ks], acc);
       }
       bias = *reinterpret_cast<const f32x4*>(&sm.u.a.rbias[w][t % kRing][4 * g]);
     } else {
