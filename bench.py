@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode", "decode_batch", "mx_sampled", "ablation", "tiny"])
     ap.add_argument("--records", type=int, default=None)
+    ap.add_argument("--kv", default="int4", choices=["int4", "bf16"], help="decode_batch: packed 4-bit or bf16 K/V")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-rows", action="store_true", help="skip the full-row sub-measurement of the default run")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -399,6 +400,23 @@ def decode_batch_inputs(n_seq: int, r_window: int, dev):
     return Q, packed
 
 
+def decode_batch_bf16_inputs(n_seq: int, dev):
+    """The batched decode step's sequences with bf16 K/V (no packing): Q [n_seq, 16, 1, 128], K, V
+    [n_seq, 2, L, 128]."""
+    import torch
+
+    from quantized_kv_amd import inputs
+
+    L, hkv, hq = inputs.DECODE_L, inputs.DECODE_HKV, inputs.DECODE_HQ
+    Q = torch.empty((n_seq, hq, 1, 128), dtype=torch.bfloat16, device=dev)
+    K = torch.empty((n_seq, hkv, L, 128), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    for b in range(n_seq):
+        q, k, v = inputs.decode_inputs(DECODE_BATCH_SEED0 + b, mq=1)
+        Q[b], K[b], V[b] = q.to(dev), k.to(dev), v.to(dev)
+    return Q, K, V
+
+
 def run_decode_batch(args):
     """Decode-shaped attention over the packed 4-bit cache: one query position per sequence, many
     sequences per launch, so every byte of the packed K/V is read once per step (HBM-bound)."""
@@ -411,12 +429,20 @@ def run_decode_batch(args):
     L, R = inputs.DECODE_L, 16
     n_seq = args.records or DECODE_BATCH
     t_gen = time.time()
-    Q, packed = decode_batch_inputs(n_seq, R, dev)
+    if args.kv == "bf16":
+        Q, K, V = decode_batch_bf16_inputs(n_seq, dev)
+        packed = None
+    else:
+        Q, packed = decode_batch_inputs(n_seq, R, dev)
     gen_s = time.time() - t_gen
     stream = torch.cuda.current_stream()
-    res = B.run(Q, None, want=("top32", "o", "region_mass"), attend=True, mode=B.MODE_INT4KV, kv_packed=packed,
-                r_window=R, n_k=L, n_heads_kv=inputs.DECODE_HKV, causal=True, q_pos0=L - 1,
-                region_bounds=[0, L - R, L])
+    if args.kv == "bf16":
+        res = B.run(Q, K, V, want=("top32", "o", "region_mass"), attend=True, causal=True, q_pos0=L - 1,
+                    region_bounds=[0, L - R, L])
+    else:
+        res = B.run(Q, None, want=("top32", "o", "region_mass"), attend=True, mode=B.MODE_INT4KV, kv_packed=packed,
+                    r_window=R, n_k=L, n_heads_kv=inputs.DECODE_HKV, causal=True, q_pos0=L - 1,
+                    region_bounds=[0, L - R, L])
     a = res["_keepalive"][0]
     ms = time_it(lambda: B.kvprof_attend(a, stream), args.steps, args.warmup, stream)
     # the codec on its own: pack 32 sequences' K/V (bf16 in, blobs out)
@@ -425,13 +451,16 @@ def run_decode_batch(args):
     ms_pack = time_it(lambda: B.kvprof_pack_int4kv(kc, vc, R), args.steps, args.warmup, stream)
     pack_bytes = kc.numel() * 2 * 2 + kc.shape[0] * B.kvprof_int4kv_bytes(L, 128, R)
     rows = Q.shape[0] * Q.shape[1]
-    # algorithmic bytes: every packed blob once, the Q rows, and the outputs (O, top-32, 2 region masses)
-    nbytes = packed.numel() + Q.numel() * 2 + rows * (128 * 4 + 32 * 4 + 2 * 4)
+    # algorithmic bytes: every packed blob (or bf16 K and V) once, the Q rows, and the outputs (O, top-32,
+    # 2 region masses)
+    kv_bytes = packed.numel() if packed is not None else (K.numel() + V.numel()) * 2
+    nbytes = kv_bytes + Q.numel() * 2 + rows * (128 * 4 + 32 * 4 + 2 * 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"metric": METRIC, "value": round(rows / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-            "config": {"workload": "batched decode step over 4-bit KV, R=16", "sequences": n_seq,
+            "config": {"workload": ("batched decode step over 4-bit KV, R=16" if args.kv == "int4" else
+                                    "batched decode step over bf16 KV"), "sequences": n_seq,
                        "q_heads": inputs.DECODE_HQ, "kv_heads": inputs.DECODE_HKV, "keys": L, "positions": 1},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes},

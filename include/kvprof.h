@@ -244,7 +244,10 @@ int kvprof_row_stats(const kvprof_args* a, void* stream);
  * indices and region masses give recall@32 and the recent-window mass). o is required.
  * Head dimension 128 gives every statistic. Head dimensions 32 and 64 (the residual-window study runs at
  * 32) give o, row_max, row_lse, region_mass, support and the histograms (modes BF16 and INT4KV, any
- * n_k < 65536); other outputs return EUNSUPPORTED. kvprof_row_stats accepts the same short heads. */
+ * n_k < 65536); other outputs return EUNSUPPORTED. kvprof_row_stats accepts the same short heads.
+ * Decode-shaped calls — at most 16 query rows per KV head ((n_heads_q / n_heads_kv) * n_q <= 16), modes
+ * BF16 and INT4KV, outputs among o, top32, region_mass, row_max and row_lse only — accept n_k up to
+ * 8,192: rows longer than KVPROF_MAX_KEYS are split over several workgroups and merged by log-sum-exp. */
 int kvprof_attend(const kvprof_args* a, void* stream);
 
 /* Colour-range clip of a heatmap ("Catnip Week 10 KV Cache Attention Study", Figure 10: maps clipped at

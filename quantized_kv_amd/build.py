@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvprof.so")
 SOURCES = ["rowstats_mx.hip", "rowstats_int4.hip", "rowstats_bf16.hip", "codecs.hip", "rowstats.hip",
-           "finalize.hip", "ablation.hip", "maps.hip", "attend_short.hip", "api.hip"]
+           "finalize.hip", "ablation.hip", "maps.hip", "attend_short.hip", "decode.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -56,13 +56,27 @@ int check_mx_shape(const void* x, const void* codes, const void* scales, int64_t
 
 struct Workspace {
   size_t q_mx = 0, k_mx = 0, frame = 0, support = 0, region = 0, redo = 0;
-  size_t lse = 0, kpart = 0, kmass = 0, ppart = 0, total = 0;
+  size_t lse = 0, kpart = 0, kmass = 0, ppart = 0, dec = 0, decflags = 0, total = 0;
 };
 
 int64_t total_rows(const kvprof_args* a) { return (int64_t)a->n_batch * a->n_heads_q * a->n_q; }
 
 bool wants_key_mass(const kvprof_args* a) { return a->key_mass || a->spatial || a->spatial_mean; }
 bool wants_maps(const kvprof_args* a) { return wants_key_mass(a) || a->pooled || a->p_row_out; }
+
+// Decode-shaped calls (at most 16 query rows per KV head, attention outputs only) whose rows are longer
+// than one workgroup holds on chip (KVPROF_MAX_KEYS) take the split-key kernels, which spread a
+// sequence's keys over several workgroups; shorter rows stay on the row kernel, which is faster there.
+bool decode_path(const kvprof_args* a) {
+  if (a->d != KVPROF_HEAD_DIM || a->mode == KVPROF_MODE_MXFP8 || a->n_heads_kv <= 0) return false;
+  const int64_t rows_per_kv = (int64_t)(a->n_heads_q / a->n_heads_kv) * a->n_q;
+  if (rows_per_kv < 1 || rows_per_kv > 16) return false;
+  if (a->n_k <= KVPROF_MAX_KEYS || a->n_k > kvp::kDecMaxKeys) return false;
+  if (a->support || a->top_mass || a->strict_zero || a->frame_mass || a->heatmap || a->heatmap_mean || a->hist)
+    return false;
+  if (a->tv_qk || a->argmax || a->argmax_ref || a->p_zero_frac || a->tv_p || a->p_rowsum || wants_maps(a)) return false;
+  return true;
+}
 
 Workspace workspace_layout(const kvprof_args* a) {
   Workspace w;
@@ -106,6 +120,15 @@ Workspace workspace_layout(const kvprof_args* a) {
       off += round256((size_t)rows * a->pool_w * 4);
     }
   }
+  if (rows > 0 && decode_path(a)) {  // split-key decode: chunk records and per-row fallback flags
+    const int64_t nch = (a->n_k + kvp::kDecChunk - 1) / kvp::kDecChunk;
+    w.dec = off;
+    off += round256((size_t)a->n_batch * a->n_heads_kv * nch * 16 * kvp::kDecRecWords * 4);
+    w.decflags = off;
+    off += round256((size_t)rows * 4);
+    w.total = off;
+    return w;
+  }
   if (rows > 0 && a->n_heads_kv > 0) {  // redo list of the row kernel
     w.redo = off;
     const long long nb = kvp::row_blocks(a->n_batch, a->n_heads_kv, (a->n_heads_q / a->n_heads_kv) * a->n_q);
@@ -135,7 +158,9 @@ int validate_args(const kvprof_args* a, bool need_o) {
     return fail(KVPROF_ESHAPE, "n_heads_q (%d) must be a multiple of n_heads_kv (%d)", a->n_heads_q, a->n_heads_kv);
   if (a->n_k < 1) return fail(KVPROF_ESHAPE, "n_k must be >= 1");
   if (a->n_k >= 65536) return fail(KVPROF_EUNSUPPORTED, "n_k must be < 65536");
-  const int maxk = short_head ? 65535 : (a->mode == KVPROF_MODE_MXFP8 ? KVPROF_MAX_KEYS_MX : KVPROF_MAX_KEYS);
+  const int maxk = short_head ? 65535
+                             : (decode_path(a) ? kvp::kDecMaxKeys
+                                               : (a->mode == KVPROF_MODE_MXFP8 ? KVPROF_MAX_KEYS_MX : KVPROF_MAX_KEYS));
   if (a->n_k > maxk) return fail(KVPROF_EUNSUPPORTED, "n_k = %d exceeds the %d keys a row can hold in this mode", a->n_k, maxk);
   if (!std::isfinite(a->scale)) return fail(KVPROF_EINVAL, "scale must be finite");
   if (a->causal != 0 && a->causal != 1) return fail(KVPROF_EINVAL, "causal must be 0 or 1");
@@ -299,12 +324,54 @@ int run_short(const kvprof_args* a, hipStream_t s) {
   return ok();
 }
 
+int run_decode(const kvprof_args* a, hipStream_t s) {
+  const Workspace ws = workspace_layout(a);
+  char* wsb = reinterpret_cast<char*>(a->workspace);
+  kvp::DecParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.n_batch = a->n_batch;
+  p.n_heads_q = a->n_heads_q;
+  p.n_heads_kv = a->n_heads_kv;
+  p.n_q = a->n_q;
+  p.n_k = a->n_k;
+  p.group = a->n_heads_q / a->n_heads_kv;
+  p.rows_per_kv = p.group * a->n_q;
+  p.causal = a->causal;
+  p.q_pos0 = a->q_pos0;
+  p.scale_log2 = a->scale * 1.44269504088896340736f;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.key_bias = a->key_bias;
+  p.n_regions = a->n_regions;
+  for (int i = 0; i <= a->n_regions && a->n_regions > 0; ++i) p.region_bounds[i] = a->region_bounds[i];
+  p.n_chunks = (a->n_k + kvp::kDecChunk - 1) / kvp::kDecChunk;
+  p.part = reinterpret_cast<float*>(wsb + ws.dec);
+  p.flags = reinterpret_cast<int*>(wsb + ws.decflags);
+  p.o = a->o;
+  p.region_mass = a->region_mass;
+  p.row_max = a->row_max;
+  p.row_lse = a->row_lse;
+  p.top32 = a->top32;
+  int ksrc = kvp::KSRC_BF16;
+  if (a->mode == KVPROF_MODE_INT4KV) {
+    ksrc = kvp::KSRC_INT4;
+    p.kv_packed = reinterpret_cast<const uint8_t*>(a->kv_packed);
+    p.blob_bytes = kvprof_int4kv_bytes(a->n_k, a->d, a->r_window);
+    p.r_window = a->r_window;
+    p.k = nullptr;
+    p.v = nullptr;
+  }
+  return launched(kvp::launch_decode(p, ksrc, s), "split-key decode");
+}
+
 int run_rows(const kvprof_args* a, void* stream, bool need_o) {
   int st = validate_args(a, need_o);
   if (st != KVPROF_OK) return st;
   const int64_t rows = total_rows(a);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (a->d != KVPROF_HEAD_DIM) return run_short(a, s);
+  if (rows > 0 && decode_path(a)) return run_decode(a, s);
   const bool mx = a->mode == KVPROF_MODE_MXFP8;
   const int tpw = kvp::row_stats_tpw_for(a->n_k, mx);
   if (tpw < 0) return fail(KVPROF_EUNSUPPORTED, "n_k = %d is not supported", a->n_k);

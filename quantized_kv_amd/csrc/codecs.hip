@@ -276,6 +276,87 @@ __global__ void pack_v_kernel(const uint16_t* __restrict__ v, int heads, int64_t
   }
 }
 
+// One workgroup per (head, 32-token group) for d in {32, 64, 128, 256}: the group's K and V rows come in
+// with 16-byte loads (a K group is 32 consecutive token rows, so both tiles are contiguous in memory),
+// then K's per-channel (scale, min) over the group's valid tokens, K's codes four bytes (8 channels of
+// one token) per store, and V's per-token 32-feature groups. The arithmetic is int4_meta / int4_code,
+// as in pack_k_kernel and pack_v_kernel.
+template <int D>
+__global__ __launch_bounds__(256) void pack_group_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                         int64_t N, int R, uint8_t* __restrict__ out, size_t blob) {
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  __shared__ uint16_t kt[32][D + 8];
+  __shared__ uint16_t vt[32][D + 8];
+  __shared__ Int4Meta kmeta[D];
+  const Int4Layout L = int4_layout(N, D, R);
+  const int64_t g = blockIdx.x % L.G;
+  const int h = (int)(blockIdx.x / L.G);
+  const int64_t t0 = g * 32;
+  const int nt = (int)min((int64_t)32, L.n - t0);  // valid tokens of the group
+  const int tid = threadIdx.x;
+  const uint16_t* kh = k + ((int64_t)h * N + t0) * D;
+  const uint16_t* vh = v + ((int64_t)h * N + t0) * D;
+  for (int c = tid; c < 32 * CH; c += 256) {
+    const int tok = c / CH, off = (c % CH) * 8;
+    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+    if (tok < nt) {
+      a = *reinterpret_cast<const uint4*>(kh + (int64_t)tok * D + off);
+      b = *reinterpret_cast<const uint4*>(vh + (int64_t)tok * D + off);
+    }
+    *reinterpret_cast<uint4*>(&kt[tok][off]) = a;
+    *reinterpret_cast<uint4*>(&vt[tok][off]) = b;
+  }
+  __syncthreads();
+  uint8_t* ob = out + (size_t)h * blob;
+  for (int c = tid; c < D; c += 256) {
+    float lo = INFINITY, hi = -INFINITY;
+    for (int tok = 0; tok < nt; ++tok) {
+      const float xv = bf16_to_f32(kt[tok][c]);
+      lo = fminf(lo, xv);
+      hi = fmaxf(hi, xv);
+    }
+    const Int4Meta mt = int4_meta(lo, hi);
+    kmeta[c] = mt;
+    _Float16* meta = reinterpret_cast<_Float16*>(ob + L.km) + (g * D + c) * 2;
+    meta[0] = mt.s;
+    meta[1] = mt.m;
+  }
+  __syncthreads();
+  // K codes: token tok, channels 8q .. 8q+7 -> one 32-bit word (pad tokens code 0)
+  for (int it = tid; it < 32 * CH; it += 256) {
+    const int tok = it / CH, q = it % CH;
+    uint32_t wd = 0u;
+    if (tok < nt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wd |= int4_code(bf16_to_f32(kt[tok][8 * q + e]), kmeta[8 * q + e]) << (4 * e);
+    }
+    *reinterpret_cast<uint32_t*>(ob + L.kc + (t0 + tok) * (D / 2) + 4 * q) = wd;
+  }
+  // V: token tok, 32-feature group f -> (scale, min) and 16 bytes of codes
+  for (int it = tid; it < nt * (D / 32); it += 256) {
+    const int tok = it / (D / 32), f = it % (D / 32);
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll 8
+    for (int c = 0; c < 32; ++c) {
+      const float xv = bf16_to_f32(vt[tok][32 * f + c]);
+      lo = fminf(lo, xv);
+      hi = fmaxf(hi, xv);
+    }
+    const Int4Meta mt = int4_meta(lo, hi);
+    _Float16* meta = reinterpret_cast<_Float16*>(ob + L.vm) + ((t0 + tok) * (D / 32) + f) * 2;
+    meta[0] = mt.s;
+    meta[1] = mt.m;
+    uint32_t* cw = reinterpret_cast<uint32_t*>(ob + L.vc + (t0 + tok) * (D / 2) + 16 * f);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t wd = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wd |= int4_code(bf16_to_f32(vt[tok][32 * f + 8 * q + e]), mt) << (4 * e);
+      cw[q] = wd;
+    }
+  }
+}
+
 // Header and the float32 residual window (bf16 -> fp32 is exact).
 __global__ void pack_tail_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                  int heads, int64_t N, int d, int R, uint8_t* __restrict__ out,
@@ -536,8 +617,20 @@ hipError_t launch_pack_int4kv(const uint16_t* k, const uint16_t* v, int heads, i
   int64_t nk = (int64_t)heads * L.G * (d / 2);
   int64_t nv = (int64_t)heads * L.n * (d / 32);
   int64_t nt = (int64_t)heads * ((int64_t)R * d + 1);
-  if (nk > 0) hipLaunchKernelGGL(pack_k_kernel, dim3(grid_for(nk, 128)), dim3(128), 0, s, k, heads, N, d, R, out, blob);
-  if (nv > 0) hipLaunchKernelGGL(pack_v_kernel, dim3(grid_for(nv, 128)), dim3(128), 0, s, v, heads, N, d, R, out, blob);
+  const int64_t nwg = (int64_t)heads * L.G;
+  const bool grouped = (d == 32 || d == 64 || d == 128 || d == 256) && ((uintptr_t)k & 15) == 0 &&
+                       ((uintptr_t)v & 15) == 0 && ((uintptr_t)out & 3) == 0 && nwg <= 0x7fffffff;
+  if (grouped) {
+    if (nwg > 0) {
+      if (d == 32) hipLaunchKernelGGL(pack_group_kernel<32>, dim3((unsigned)nwg), dim3(256), 0, s, k, v, N, R, out, blob);
+      if (d == 64) hipLaunchKernelGGL(pack_group_kernel<64>, dim3((unsigned)nwg), dim3(256), 0, s, k, v, N, R, out, blob);
+      if (d == 128) hipLaunchKernelGGL(pack_group_kernel<128>, dim3((unsigned)nwg), dim3(256), 0, s, k, v, N, R, out, blob);
+      if (d == 256) hipLaunchKernelGGL(pack_group_kernel<256>, dim3((unsigned)nwg), dim3(256), 0, s, k, v, N, R, out, blob);
+    }
+  } else {
+    if (nk > 0) hipLaunchKernelGGL(pack_k_kernel, dim3(grid_for(nk, 128)), dim3(128), 0, s, k, heads, N, d, R, out, blob);
+    if (nv > 0) hipLaunchKernelGGL(pack_v_kernel, dim3(grid_for(nv, 128)), dim3(128), 0, s, v, heads, N, d, R, out, blob);
+  }
   hipLaunchKernelGGL(pack_tail_kernel, dim3(grid_for(nt, 256)), dim3(256), 0, s, k, v, heads, N, d, R, out, blob);
   return hipGetLastError();
 }

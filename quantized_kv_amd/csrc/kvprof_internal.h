@@ -118,6 +118,39 @@ struct ShortParams {
 // d = 32 or 64; ksrc = KSRC_BF16 or KSRC_INT4.
 hipError_t launch_attend_short(const ShortParams& p, int d, int ksrc, hipStream_t s);
 
+// ---- split-key decode (decode.hip) ------------------------------------------------------------------
+
+constexpr int kDecChunk = 1024;      // keys per workgroup
+constexpr int kDecMaxChunks = 8;     // so n_k <= 8192
+constexpr int kDecMaxKeys = kDecChunk * kDecMaxChunks;
+// per (batch, KV head, chunk, row slot) record in the workspace, in 32-bit words
+constexpr int kDecM = 0, kDecZ = 1, kDecFlag = 2, kDecReg = 3, kDecO = kDecReg + KVPROF_MAX_REGIONS,
+              kDecCu = kDecO + 128, kDecCj = kDecCu + 32, kDecRecWords = 208;
+static_assert(kDecCj + 32 <= kDecRecWords, "decode record");
+
+struct DecParams {
+  int n_batch, n_heads_q, n_heads_kv, n_q, n_k;
+  int group, rows_per_kv, causal;
+  long long q_pos0;
+  float scale_log2;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint8_t* kv_packed;
+  size_t blob_bytes;
+  int r_window;
+  const float* key_bias;
+  int n_regions;
+  int region_bounds[KVPROF_MAX_REGIONS + 1];
+  int n_chunks;
+  float* part;   // workspace: n_batch * n_heads_kv * n_chunks * 16 records
+  int* flags;    // workspace: [rows] 1 = the row's top-32 needs the exact fallback
+  float *o, *region_mass, *row_max, *row_lse;
+  int* top32;
+};
+
+hipError_t launch_decode(const DecParams& p, int ksrc, hipStream_t s);
+
 // ---- probability maps (maps.hip) -------------------------------------------------------------------
 
 constexpr int kMaxPoolW = 128;  // widest pooled map (four 32-column MFMA blocks)
