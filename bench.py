@@ -24,6 +24,12 @@ reports, inputs already resident in HBM:
              the sink, the recent region and all history dropped (P renormalised over the kept keys),
              each compared with the full O by per-row relative L2 and cosine.
 
+* maps     : the sampled workload with the spatial maps added (key masses, sink / recent / current
+             spatial maps per head and per record, the 64 x 96 pooled map per head, one query's
+             probabilities and its 99.5th-percentile clip); reports the maps' own time beside the
+             statistics-only call.
+* p2       : the fixed-budget residual-window protocol at head dimension 32 (18 inputs x R in
+             {0, 16, 64}: pack, 4-bit attention, bf16 reference, comparison); launch-latency-bound.
 * tiny     : the three 128 x 128 variants (clean, early_focus, recent_focus) with every statistic and
              O in one call, and the same rows in MXFP8 mode (pack + statistics): launch-latency-bound,
              reported as microseconds per call with no roofline claim.
@@ -51,7 +57,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode", "decode_batch", "mx_sampled", "ablation", "tiny"])
+    ap.add_argument("--workload", default="sampled", choices=["sampled", "full_rows", "decode", "decode_batch", "mx_sampled", "ablation", "tiny",
+                                                         "maps", "p2"])
     ap.add_argument("--records", type=int, default=None)
     ap.add_argument("--kv", default="int4", choices=["int4", "bf16"], help="decode_batch: packed 4-bit or bf16 K/V")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -581,6 +588,90 @@ def run_ablation(args):
     return out
 
 
+def run_maps(args):
+    """The sampled workload's statistics with and without the spatial maps; the difference is the maps'
+    second pass over K (maps_kernel) and their small reductions."""
+    import torch
+
+    from quantized_kv_amd import binding as B
+    from quantized_kv_amd import inputs
+
+    dev = torch.device("cuda:0")
+    n_rec = args.records or inputs.N_RECORDS
+    Q, K = video_inputs(n_rec, True, dev)
+    Bn, H, Mq, _ = Q.shape
+    Sk = K.shape[2]
+    rows = Bn * H * Mq
+    bias = torch.from_numpy(inputs.video_key_bias()).to(dev)
+    kw = dict(scale=128 ** -0.5, key_bias=bias, region_bounds=inputs.VIDEO_REGION_BOUNDS, frame_len=inputs.LF_TOKENS,
+              n_frames=inputs.N_KEY_FRAMES)
+    want = ("support", "top_mass", "top32", "strict_zero", "region_mass", "frame_mass", "row_max", "row_lse")
+    stream = torch.cuda.current_stream()
+    plain = B.run(Q, K, want=want, **kw)["_keepalive"][0]
+    res = B.run(Q, K, want=want, maps_want=("key_mass", "spatial", "spatial_mean"), pool=(64, 96), p_row=23 * 96 + 50,
+                **kw)
+    full = res["_keepalive"][0]
+    p_row = res["p_row_out"][: inputs.N_KEY_FRAMES * inputs.LF_TOKENS]
+    clip = torch.empty(1, dtype=torch.float32, device=dev)
+    clipped = torch.empty_like(p_row)
+    lib, sp = B.load(), stream.cuda_stream
+
+    def step():
+        B.kvprof_row_stats(full, stream)
+        lib.kvprof_percentile_clip(p_row.data_ptr(), p_row.numel(), 99.5, B.QUANTILE_SAMPLE_CAP, clip.data_ptr(),
+                                   clipped.data_ptr(), sp)
+
+    ms = time_it(step, args.steps, args.warmup, stream)
+    ms_plain = time_it(lambda: B.kvprof_row_stats(plain, stream), args.steps, 1, stream)
+    ms_maps = ms - ms_plain
+    # the maps pass: K once per (record, head) per 32-row block group of that head (read through L2), the
+    # row lse, and the partial outputs written and reduced
+    kbytes = K.numel() * 2 + Q.numel() * 2 + rows * 4
+    gbs = kbytes / (ms_maps * 1e-3) / 1e9
+    return {"metric": METRIC, "value": round(rows / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "video steady chunk, sampled queries, statistics + spatial maps", "records": Bn,
+                       "heads": H, "queries_per_head": Mq, "keys": Sk, "pool": [64, 96]},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": kbytes,
+                         "kernel": "maps pass (call with maps minus call without)"},
+            "maps_ms": round(ms_maps, 4), "statistics_ms": round(ms_plain, 4)}
+
+
+def run_p2(args):
+    """The residual-window protocol's 54 comparisons through the C ABI, timed as a whole."""
+    import torch
+
+    from quantized_kv_amd import inputs, p2
+
+    dev = torch.device("cuda:0")
+    data = [(s, n, v, [t.to(dev) for t in inputs.p2_inputs(s, n, v)]) for v in inputs.TINY_VARIANTS
+            for n in inputs.P2_LENGTHS for s in inputs.P2_SEEDS]
+    for _ in range(max(1, args.warmup)):
+        for _, _, _, (q, k, v) in data:
+            p2.run_case(q, k, v)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    recs = []
+    for _ in range(args.steps):
+        recs = [(vv, p2.run_case(q, k, v)) for _, _, vv, (q, k, v) in data]
+    dt = (time.perf_counter() - t0) / args.steps
+    summary = {}
+    for vv in inputs.TINY_VARIANTS:
+        rs = [r for name, r in recs if name == vv]
+        summary[vv] = {"rel_l2": {w: round(sum(r["rel_l2"][w] for r in rs) / len(rs), 5) for w in inputs.P2_WINDOWS},
+                       "recent_mass": {w: round(sum(r["recent_mass"][w] for r in rs) / len(rs), 5)
+                                       for w in inputs.P2_WINDOWS}}
+    return {"metric": METRIC, "value": round(54 / dt, 1), "unit": "comparisons/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "residual-window protocol, 18 inputs x R in {0, 16, 64}, head dim 32",
+                       "lengths": list(inputs.P2_LENGTHS), "seeds": list(inputs.P2_SEEDS)},
+            "roofline": None, "note": "launch-latency-bound (host-synchronised per input); no roofline claimed",
+            "summary": summary}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -604,6 +695,10 @@ def main():
         out = run_mx(args)
     elif args.workload == "ablation":
         out = run_ablation(args)
+    elif args.workload == "maps":
+        out = run_maps(args)
+    elif args.workload == "p2":
+        out = run_p2(args)
     else:
         out = run_video(args, sampled=args.workload == "sampled")
         if args.workload == "sampled" and not args.no_full_rows:
