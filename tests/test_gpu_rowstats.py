@@ -184,3 +184,25 @@ def test_video_shape_ties_and_redo(kvprof_lib):
     ref = O.row_stats(inputs.bf16_values(Q)[0, 0], inputs.bf16_values(K)[0, 0], scale=128 ** -0.5,
                       key_bias=bias, **VIDEO_KW)
     P.check_rows(g, ref)
+
+
+def test_video_top_mass_interpolation_bound(kvprof_lib):
+    """The kernel's in-bin estimate of the top-1/5/10 % masses is used only when its error bound is
+    within 4e-4; on every row of a full sampled record (32 heads x 96 queries) the masses stay within
+    that bound (plus float32 summation) of the oracle's exact rank definition."""
+    rec = inputs.video_record(0, with_v=False, sampled=True)
+    bias = inputs.video_key_bias()
+    print("top-f mass bound, video record 0", flush=True)
+    g = B.run(rec.q[None].to(DEV), rec.k[None].to(DEV), want=("top_mass",), scale=128 ** -0.5,
+              key_bias=torch.from_numpy(bias).to(DEV), **VIDEO_KW)
+    torch.cuda.synchronize()
+    got = g["top_mass"].cpu().numpy().reshape(32, 96, 3)
+    qv, kv = inputs.bf16_values(rec.q), inputs.bf16_values(rec.k)
+    n = kv.shape[1]
+    worst = 0.0
+    for h in range(32):
+        p = O.probabilities(qv[h], kv[h], scale=128 ** -0.5, key_bias=bias)
+        want = np.array([[O.top_mass(p[i], n, pct) for pct in O.TOP_PCTS] for i in range(p.shape[0])])
+        worst = max(worst, float(np.max(np.abs(got[h] - want))))
+    print(f"max |top_mass - oracle| = {worst:.2e}", flush=True)
+    assert worst <= 4e-4 + 5e-6
