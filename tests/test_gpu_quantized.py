@@ -224,3 +224,39 @@ def test_attend_int4_decode_batch(kvprof_lib):
                 P.check_top32(g["top32"][sl], ref["scores"], ref["n_visible"])
                 P.check_o(g["o"][sl], ref["o"])
                 P.check_close("recent mass", g["region_mass"][sl, 1], ref["region_mass"][:, 1], atol=P.MASS_ATOL)
+
+
+def test_mxfp8_blocks_below_bf16_range(kvprof_lib):
+    """MXFP8 blocks whose E8M0 exponent sits at the bottom of its range (query rows and keys scaled by
+    1e-36, so the E4M3 subnormals times the block scale lie below bf16's smallest subnormal) next to
+    ordinary rows and keys: the kernel takes MX products on bf16-decoded operands, which cannot hold
+    those values, and every statistic must still agree with the oracle's exact decode to tolerance."""
+    rng = np.random.default_rng(29)
+    Sk, Mq = 2048, 32
+    k = rng.standard_normal((1, 1, Sk, 128)).astype(np.float32)
+    q = rng.standard_normal((1, 1, Mq, 128)).astype(np.float32) * 1.5
+    q[0, 0, 0:8] *= 1e-36
+    k[0, 0, 500:564] *= 1e-36
+    k[0, 0, 1000:1032] *= 1e-30
+    Q, K = inputs.to_bf16(q), inputs.to_bf16(k)
+    signs = inputs.hadamard_signs(4)
+    sg = torch.from_numpy(signs).to(DEV)
+    qd, kd = Q.to(DEV), K.to(DEV)
+    print("MXFP8 tiny blocks", flush=True)
+    qc, qs = B.kvprof_pack_mxfp8(qd.reshape(-1, 128), sg)
+    kc, ks = B.kvprof_pack_mxfp8(kd.reshape(-1, 128), sg)
+    assert int(qs.cpu().numpy()[:8].min()) <= 1  # E8M0 bytes: exponent + 127
+    kw = dict(region_bounds=[0, 512, 1024, Sk], frame_len=128, n_frames=16)
+    want = ("support", "top_mass", "top32", "strict_zero", "region_mass", "frame_mass", "tv_qk", "argmax",
+            "argmax_ref", "p_zero_frac", "tv_p", "p_rowsum")
+    g = _np(B.run(qd, kd, want=want, mode=B.MODE_MXFP8, q_codes=qc, q_scales=qs, k_codes=kc, k_scales=ks,
+                  scale=128 ** -0.5, **kw))
+    torch.cuda.synchronize()
+    ref = O.mx_row_stats(inputs.bf16_values(Q)[0, 0], inputs.bf16_values(K)[0, 0], signs, scale=128 ** -0.5, **kw)
+    P.check_rows(g, ref)
+    P.check_close("tv_qk", g["tv_qk"], ref["tv_qk"], atol=P.MASS_ATOL)
+    P.check_close("tv_p", g["tv_p"], ref["tv_p"], atol=P.MASS_ATOL)
+    P.check_close("p_rowsum", g["p_rowsum"], ref["p_rowsum"], atol=P.MASS_ATOL)
+    _check_zero_frac(g["p_zero_frac"], ref["p"], Sk)
+    _check_argmax(g["argmax"], ref["scores"], "argmax")
+    _check_argmax(g["argmax_ref"], ref["ref_scores"], "argmax_ref")
