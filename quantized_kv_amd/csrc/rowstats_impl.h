@@ -112,6 +112,7 @@ struct Smem {
   float red_c[NW][ROWS];
   float segpart[NW][ROWS][kSegPerWave];
   float segmass[ROWS][kMaxSeg];
+  signed char sreg[kMaxSeg], sfr[kMaxSeg];  // region and frame of each segment
   int cs0[NW];
   float r_z[ROWS], r_e[ROWS], r_m[ROWS], r_mn[ROWS], r_T[ROWS], r_k8[ROWS];
   int rfb[ROWS];  // 1: the row's histogram is redone over every visible key
@@ -408,6 +409,39 @@ __device__ __forceinline__ float interp_mass(const TState& ts, float k8, float z
   return ((float)ts.mass_before + share * (float)ts.mass_in) / z;
 }
 
+// Inclusive prefix sums over the 64 lanes of a wave (all lanes active): Hillis-Steele steps inside
+// each row of 16 lanes on DPP row shifts (lanes without a source add 0), then the totals of the lower
+// rows, read from lanes 15, 31 and 47.
+__device__ __forceinline__ unsigned dpp_shr(unsigned x, int sh) {
+  switch (sh) {
+    case 1: return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);
+    case 2: return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);
+    case 4: return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);
+    default: return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);
+  }
+}
+__device__ __forceinline__ unsigned wave_scan_u32(unsigned x, int lane) {
+#pragma unroll
+  for (int sh = 1; sh < 16; sh <<= 1) x += dpp_shr(x, sh);
+  const unsigned t0 = (unsigned)__builtin_amdgcn_readlane((int)x, 15);
+  const unsigned t1 = (unsigned)__builtin_amdgcn_readlane((int)x, 31);
+  const unsigned t2 = (unsigned)__builtin_amdgcn_readlane((int)x, 47);
+  return x + (lane >= 16 ? t0 : 0u) + (lane >= 32 ? t1 : 0u) + (lane >= 48 ? t2 : 0u);
+}
+__device__ __forceinline__ unsigned long long wave_scan_u64(unsigned long long x, int lane) {
+#pragma unroll
+  for (int sh = 1; sh < 16; sh <<= 1) {
+    const unsigned lo = dpp_shr((unsigned)x, sh), hi = dpp_shr((unsigned)(x >> 32), sh);
+    x += ((unsigned long long)hi << 32) | lo;
+  }
+  auto at = [&](int l) {
+    return ((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(x >> 32), l) << 32) |
+           (unsigned)__builtin_amdgcn_readlane((int)(unsigned)x, l);
+  };
+  const unsigned long long t0 = at(15), t1 = at(31), t2 = at(47);
+  return x + (lane >= 16 ? t0 : 0ull) + (lane >= 32 ? t1 : 0ull) + (lane >= 48 ? t2 : 0ull);
+}
+
 // Per-row scan of the level-1 histogram by one wave (lane holds bins 4*lane..4*lane+3): locates, for
 // every target of the row, the bin that holds its rank. A row whose histogram holds no more keys than
 // its deepest target is marked for a redo over every visible key.
@@ -431,17 +465,9 @@ __device__ void scan_row(SM& sm, int row, int lane) {
   }
   const unsigned lc = c[0] + c[1] + c[2] + c[3];
   const unsigned long long lm = m[0] + m[1] + m[2] + m[3];
-  unsigned ic = lc;
-  unsigned long long im = lm;
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned tc = __shfl_up(ic, o);
-    const unsigned long long tm = __shfl_up(im, o);
-    if (lane >= o) {
-      ic += tc;
-      im += tm;
-    }
-  }
-  const unsigned total = __shfl(ic, 63);
+  const unsigned ic = wave_scan_u32(lc, lane);
+  const unsigned long long im = wave_scan_u64(lm, lane);
+  const unsigned total = (unsigned)__builtin_amdgcn_readlane((int)ic, 63);
   const unsigned run = ic - lc;
   const unsigned long long mrun = im - lm;
   int redo = 0;
@@ -523,8 +549,12 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   Int4Layout L{};
   if (KSRC == KSRC_INT4) L = int4_layout(p.n_k, KVPROF_HEAD_DIM, p.r_window);
 
-  // clear the shared accumulators
+  // clear the shared accumulators; the segments' region and frame maps into LDS
   for (int i = tid; i < NW * ROWS * kSegPerWave; i += WGT) (&sm.segpart[0][0][0])[i] = 0.f;
+  if (tid < p.n_seg) {
+    sm.sreg[tid] = p.seg_region[tid];
+    sm.sfr[tid] = p.seg_frame[tid];
+  }
 
   // Q rows of the workgroup into LDS (wave 0): chunk c of row r holds dims 8c .. 8c+7
   if (w == 0) {
@@ -826,8 +856,8 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll 8
       for (int s = 0; s < p.n_seg; ++s) {
         const float x = sm.segmass[row][s];
-        ar += p.seg_region[s] == lane ? x : 0.f;
-        af += p.seg_frame[s] == lane ? x : 0.f;
+        ar += sm.sreg[s] == lane ? x : 0.f;
+        af += sm.sfr[s] == lane ? x : 0.f;
       }
       if (p.region_mass && lane < p.n_regions) p.region_mass[ri.grow * p.n_regions + lane] = ar * iz;
       if (p.frame_mass && lane < p.n_frames) p.frame_mass[ri.grow * p.n_frames + lane] = af * iz;
@@ -1048,7 +1078,23 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       const float mr = sm.r_m[row];
       const RowInfo ri = row_info(p, b, hkv, rb, row);
       const int c = min(sm.ncand[row], CAPL);
-      const int b0 = sm.ts[row][0].valid ? (int)sm.ts[row][0].prefix : -1;
+      // the row's targets (the same on every lane of the wave): those ranked exactly, their bins,
+      // ranks inside the bin, keys before the bin and fractions
+      bool ex[NT];
+      unsigned pre[NT];
+      int rrk[NT], cb[NT];
+      float fr[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const TState& ts = sm.ts[row][t];
+        ex[t] = ts.valid && !ts.interp;
+        pre[t] = ts.prefix;
+        rrk[t] = ts.target - ts.cnt_before;
+        cb[t] = ts.cnt_before;
+        fr[t] = ts.frac;
+      }
+      const int b0 = ex[0] ? (int)pre[0] : -1;
+      const bool anyf = ex[1] | ex[2] | ex[3];
       unsigned long long acc[NT] = {0ull, 0ull, 0ull, 0ull};
       for (int a = lane; a < c; a += 64) {
         const unsigned long long ka = sm.u.sel.ck[row][a];
@@ -1061,29 +1107,26 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           sm.win_u[row][slot] = ua;
           sm.win_j[row][slot] = ja;
         }
-      const float ea = __builtin_amdgcn_exp2f(fmaxf(ua + (kOff - mr), -256.f));
+        if (ex[0] && pre[0] == dga && rk <= rrk[0]) {  // ranks 0..target of the top-32 list
+          sm.win_u[row][cb[0] + rk] = ua;
+          sm.win_j[row][cb[0] + rk] = ja;
+        }
+        if (anyf) {
+          const float ea = __builtin_amdgcn_exp2f(fmaxf(ua + (kOff - mr), -256.f));
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const TState& ts = sm.ts[row][t];
-          if (!ts.valid || ts.interp || ts.prefix != dga) continue;
-          const int rr = ts.target - ts.cnt_before;
-          if (t == 0) {
-            if (rk <= rr) {  // ranks 0..target of the top-32 list
-              sm.win_u[row][ts.cnt_before + rk] = ua;
-              sm.win_j[row][ts.cnt_before + rk] = ja;
-            }
-          } else {
-            if (rk < rr) acc[t] += fixmass(ea);
-            if (rk == rr) acc[t] += fixmass(ts.frac * ea);
+          for (int t = 1; t < NT; ++t) {
+            if (!ex[t] || pre[t] != dga) continue;
+            if (rk < rrk[t]) acc[t] += fixmass(ea);
+            if (rk == rrk[t]) acc[t] += fixmass(fr[t] * ea);
           }
         }
       }
 #pragma unroll
       for (int t = 1; t < NT; ++t) {
+        if (!ex[t]) continue;  // interpolated (phase E) or a row past the end
         unsigned long long x = acc[t];
         for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-        if (lane == 0 && ri.ok && !sm.ts[row][t].interp)
-          sm.tmass[row][t - 1] = (float)(sm.ts[row][t].mass_before + x) / sm.r_z[row];
+        if (lane == 0 && ri.ok) sm.tmass[row][t - 1] = (float)(sm.ts[row][t].mass_before + x) / sm.r_z[row];
       }
     }
     __syncthreads();
@@ -1301,15 +1344,11 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         const float e_ = sm.r_e[row];
         const float H = logf(z) - kLn2 * (e_ / z);
         if (p.support) p.support[ri.grow] = expf(H) / (float)ri.nvis;
-        if (p.top_mass) {
-#pragma unroll 1
-          for (int t = 1; t < NT; ++t) {
-            const TState& ts = sm.ts[row][t];
-            float mass = sm.tmass[row][t - 1];
-            if (ts.interp) mass = interp_mass(ts, sm.r_k8[row], z);
-            p.top_mass[ri.grow * 3 + t - 1] = mass;
-          }
-        }
+      } else if (lane < NT && p.top_mass) {  // top-f mass of target t = lane
+        const TState& ts = sm.ts[row][lane];
+        const float mass = !ts.valid ? 0.f
+                           : (ts.interp ? interp_mass(ts, sm.r_k8[row], sm.r_z[row]) : sm.tmass[row][lane - 1]);
+        p.top_mass[ri.grow * 3 + lane - 1] = mass;
       }
     }
   }
