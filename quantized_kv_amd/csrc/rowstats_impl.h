@@ -1025,24 +1025,37 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       }
       int cpos = nc ? atomicAdd(&sm.ncand[r], nc) : 0;
       if (nc) {
+        // the list takes (score bits, key index) pairs here; they become rank keys below, once per
+        // listed key instead of in this pass over every key
         const int gq = opaque(g);
-        const float k8q = rc_k8(), mk8q = __fmul_rn(rc_m(), k8q);
         unsigned bits = 0u;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
-          const int j0 = kbase + tt * 16;
           if ((tt & 7) == 0) bits = sm.u.sel.gbits[tt >> 3][w][lane];
+          const unsigned jt = (unsigned)(kbase + tt * 16 + 4 * opaque(gq));
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if ((bits >> (4 * (tt & 7) + i)) & 1u) {  // (the fast path holds <= 31 + CAP < CAPL keys)
-              const float u = scr(tt, i);
-              sm.u.sel.ck[r][cpos] = rank_key(u, j0 + 4 * gq + i, bin1(u, k8q, mk8q));
+              // (the score goes through a copy: stored straight from its register it would tie that
+              // register to the index in an aligned pair, and the score registers then spill)
+              sm.u.sel.ck[r][cpos] = ((unsigned long long)(jt + i) << 32) | opaque(__float_as_uint(scr(tt, i)));
               ++cpos;
             }
           }
           cpos = opaque(cpos);
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+    }
+    __syncthreads();
+    // (score, index) pairs -> rank keys, by the wave that owns the row
+    for (int row = w; row < ROWS; row += NW) {
+      const int c = min(sm.ncand[row], CAPL);
+      const float k8q = sm.r_k8[row], mk8q = __fmul_rn(sm.r_m[row], k8q);
+      for (int a = lane; a < c; a += 64) {
+        const unsigned long long e = sm.u.sel.ck[row][a];
+        const float u = __uint_as_float((unsigned)e);
+        sm.u.sel.ck[row][a] = rank_key(u, (int)(e >> 32), bin1(u, k8q, mk8q));
       }
     }
     __syncthreads();
