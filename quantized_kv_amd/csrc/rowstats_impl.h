@@ -160,29 +160,73 @@ __device__ __forceinline__ RowInfo row_info(const RowStatsParams& p, int b, int 
   return ri;
 }
 
+// Cross-lane exchanges without LDS round trips. A permlane16 swap of x with itself leaves lane l
+// holding x of lane l and x of lane l ^ 16 in its two results (which one is which depends on the
+// row), a permlane32 swap the same for lane l ^ 32; DPP moves serve the exchanges inside a row of 16.
+// Every step combines two lanes that hold the same partial result, so all lanes end with the same
+// bits (fixed order, deterministic).
+__device__ __forceinline__ u32x2 swap16(unsigned x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return u32x2{r[0], r[1]};
+}
+__device__ __forceinline__ u32x2 swap32(unsigned x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return u32x2{r[0], r[1]};
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_mov(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i of an 8-lane half-row reads lane 7 - i
+constexpr int kDppMirror = 0x140;     // lane i of a 16-lane row reads lane 15 - i
+
 // Sum over the 4 lanes that hold one row (lanes r, r+16, r+32, r+48); same result on all four.
 __device__ __forceinline__ float row_sum4(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  u32x2 s = swap16(__float_as_uint(x));
+  x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  s = swap32(__float_as_uint(x));
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 __device__ __forceinline__ float row_max4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  u32x2 s = swap16(__float_as_uint(x));
+  x = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  s = swap32(__float_as_uint(x));
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 __device__ __forceinline__ float row_min4(float x) {
-  x = fminf(x, __shfl_xor(x, 16));
-  return fminf(x, __shfl_xor(x, 32));
+  u32x2 s = swap16(__float_as_uint(x));
+  x = fminf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  s = swap32(__float_as_uint(x));
+  return fminf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 __device__ __forceinline__ int row_isum4(int x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  u32x2 s = swap16((unsigned)x);
+  x = (int)(s[0] + s[1]);
+  s = swap32((unsigned)x);
+  return (int)(s[0] + s[1]);
 }
-// Fixed-order sum over a whole wave.
+// Sum over a whole wave (every lane must be active).
 __device__ __forceinline__ float wave_sum(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += __uint_as_float(dpp_mov<kDppXor1>(__float_as_uint(x)));
+  x += __uint_as_float(dpp_mov<kDppXor2>(__float_as_uint(x)));
+  x += __uint_as_float(dpp_mov<kDppHalfMirror>(__float_as_uint(x)));
+  x += __uint_as_float(dpp_mov<kDppMirror>(__float_as_uint(x)));
+  return row_sum4(x);
+}
+// Max / min over the 16 lanes of a row (every lane must be active).
+__device__ __forceinline__ int row16_max(int x) {
+  x = max(x, (int)dpp_mov<kDppXor1>((unsigned)x));
+  x = max(x, (int)dpp_mov<kDppXor2>((unsigned)x));
+  x = max(x, (int)dpp_mov<kDppHalfMirror>((unsigned)x));
+  return max(x, (int)dpp_mov<kDppMirror>((unsigned)x));
+}
+__device__ __forceinline__ int row16_min(int x) {
+  x = min(x, (int)dpp_mov<kDppXor1>((unsigned)x));
+  x = min(x, (int)dpp_mov<kDppXor2>((unsigned)x));
+  x = min(x, (int)dpp_mov<kDppHalfMirror>((unsigned)x));
+  return min(x, (int)dpp_mov<kDppMirror>((unsigned)x));
 }
 
 // Returns x through an empty asm statement: values derived from the copy are computed where the copy
@@ -529,11 +573,11 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
   const int nvis = me0.nvis;
   // workgroup-uniform extent of visible keys
   int kmax = nvis;
-  for (int o = 1; o < 16; o <<= 1) kmax = max(kmax, __shfl_xor(kmax, o));
+  kmax = row16_max(kmax);
   kmax = __builtin_amdgcn_readfirstlane(kmax);  // identical on every lane: keep it scalar
   // keys below kmin are visible to every row of the workgroup (rows past the end do not count)
   int kmin = me0.ok ? nvis : 0x7fffffff;
-  for (int o = 1; o < 16; o <<= 1) kmin = min(kmin, __shfl_xor(kmin, o));
+  kmin = row16_min(kmin);
   kmin = __builtin_amdgcn_readfirstlane(kmin);
 
   const size_t kvh = (size_t)b * p.n_heads_kv + hkv;
@@ -987,6 +1031,30 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         unsigned bits = 0u;
         if (only32) {
           const float lim = bq[0] < 0 ? -INFINITY : (bq[0] >= 255 ? INFINITY : (float)(bq[0] + 1));
+          // x = fma(-u, k8, m k8) does not increase with u, so where x(T) >= lim already, a key with
+          // x < lim lies above T and the threshold test is implied: one compare per key remains
+          // (the same keys as the two-test form, exactly).
+          const bool implied = !(__fmaf_rn(-Tq, k8q, mk8q) < lim);
+          if (__ballot(!implied) == 0ull) {
+            // (fresh copies of the row constants: otherwise the compiler shares values between the
+            // two forms of the loop and the score registers spill)
+            const float k8f = opaque(k8q), mk8f = opaque(mk8q), limf = opaque(lim);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const bool in = __fmaf_rn(-scr(tt, i), k8f, mk8f) < limf;
+                bits |= in ? 1u << (4 * (tt & 7) + i) : 0u;
+              }
+              if ((tt & 7) == 7 || tt == TPW - 1) {
+                sm.u.sel.gbits[tt >> 3][w][lane] = bits;
+                nc += __builtin_popcount(bits);
+                bits = 0u;
+              }
+              bits = opaque(bits);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
 #pragma unroll
           for (int tt = 0; tt < TPW; ++tt) {
 #pragma unroll
@@ -1002,6 +1070,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
             }
             bits = opaque(bits);
             __builtin_amdgcn_sched_barrier(0);
+          }
           }
         } else {
 #pragma unroll
