@@ -1661,6 +1661,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     __syncthreads();
     // R3: TV between the MX row and the reference row, and the P path
     float tv = 0.f, pz = 0.f, tvp = 0.f, psum = 0.f;
+    const float offm = kOff - rc_m(), invz = 1.f / rc_z();
 #pragma unroll
     for (int t = 0; t < TPW; t += 2) {
       const int j0 = kbase + t * 16;
@@ -1672,7 +1673,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         ref_tile_direct(j0 + 16 * h2, u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pm = __builtin_amdgcn_exp2f(fmaxf(scr(t + h2, i) + (kOff - rc_m()), -256.f)) / rc_z();
+          const float pm = __builtin_amdgcn_exp2f(fmaxf(scr(t + h2, i) + offm, -256.f)) * invz;
           pv[h2][i] = pm;
           tv += fabsf(pm - __builtin_amdgcn_exp2f(u[i] - mref) * invZr);
         }
@@ -1692,7 +1693,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           const int j = j0 + 16 * h2 + 4 * g + i;
           if (j < nvis) {
             const float pm = pv[h2][i];
-            const float ph = ldexpf(e4m3_value(e4m3_rne(ldexpf(pm, -eb))), eb);
+            const float ph = ldexpf(e4m3_grid(ldexpf(pm, -eb)), eb);
             pz += (pm > 0.f && ph == 0.f) ? 1.f : 0.f;
             tvp += fabsf(ph - pm);
             psum += ph;
