@@ -225,3 +225,30 @@ def test_video_top_mass_interpolation_bound(kvprof_lib):
         worst = max(worst, float(np.max(np.abs(got[h] - want))))
     print(f"max |top_mass - oracle| = {worst:.2e}", flush=True)
     assert worst <= 4e-4 + 5e-6
+
+
+def test_o_with_large_magnitude_v(kvprof_lib):
+    """V enters the P.V product as f16 (the header states the range limit |V| < 65520): values near the
+    top of that range, and mixed with tiny ones, still give O within tolerance of the oracle, in bf16
+    and in 4-bit mode (whose window keeps V as float32 and whose 4-bit part decodes into f16)."""
+    rng = np.random.default_rng(31)
+    Mq, Sk, R = 40, 700, 64
+    q = rng.standard_normal((1, 1, Mq, 128)).astype(np.float32)
+    k = rng.standard_normal((1, 1, Sk, 128)).astype(np.float32)
+    v = np.clip(rng.standard_normal((1, 1, Sk, 128)).astype(np.float32) * 2e4, -6e4, 6e4)
+    v[..., ::3] = np.clip(v[..., ::3] * 3.0, -6e4, 6e4)
+    v[..., 5::7] *= 1e-6
+    Q, K, V = inputs.to_bf16(q), inputs.to_bf16(k), inputs.to_bf16(v)
+    print("large-magnitude V", flush=True)
+    qv, kv, vv = inputs.bf16_values(Q)[0, 0], inputs.bf16_values(K)[0, 0], inputs.bf16_values(V)[0, 0]
+    g = _np(B.run(Q.to(DEV), K.to(DEV), V.to(DEV), want=("o",), attend=True, scale=128 ** -0.5, causal=True,
+                  q_pos0=Sk - Mq))
+    ref = O.row_stats(qv, kv, scale=128 ** -0.5, causal=True, q_pos0=Sk - Mq, v=vv)
+    P.check_o(g["o"], ref["o"])
+    packed = B.kvprof_pack_int4kv(K.reshape(1, Sk, 128).to(DEV), V.reshape(1, Sk, 128).to(DEV), R)
+    g4 = _np(B.run(Q.to(DEV), None, want=("o",), attend=True, mode=B.MODE_INT4KV, kv_packed=packed, r_window=R,
+                   n_k=Sk, n_heads_kv=1, scale=128 ** -0.5, causal=True, q_pos0=Sk - Mq))
+    torch.cuda.synchronize()
+    kh, vh = O.unpack_int4kv(O.pack_int4kv(kv, vv, R))
+    ref4 = O.row_stats(qv, kh, scale=128 ** -0.5, causal=True, q_pos0=Sk - Mq, v=vh)
+    P.check_o(g4["o"], ref4["o"])
