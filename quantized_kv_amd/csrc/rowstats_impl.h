@@ -1587,24 +1587,6 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
         u[i] = j < nvis ? fmaf(acc[i], p.scale_log2, fmaxf(bias[i] * kLog2e, kNegBig)) : -INFINITY;
       }
     };
-    // The same reference tile with direct loads (for the unrolled pass below, which the ring's
-    // prefetch chain would cost registers in).
-    auto ref_tile_direct = [&](int j0, float (&u)[4]) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (j0 < kmax) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const u32x4 kf = __builtin_amdgcn_raw_buffer_load_b128(rkr, (unsigned)((j0 + r) * KVPROF_HEAD_DIM + ks * 32 + 8 * g) * 2u, 0, 0);
-          acc = mfma_step<KSRC_BF16>(kf, sm.qs[r][ks * 4 + g], acc);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = j0 + 4 * g + i;
-        const float bb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, (unsigned)j * 4u, 0, 0));
-        u[i] = j < nvis ? fmaf(acc[i], p.scale_log2, fmaxf(bb * kLog2e, kNegBig)) : -INFINITY;
-      }
-    };
     // R1: reference max, argmax (ties to the lowest index) and normaliser in one pass: the running
     // sum is rescaled whenever the running max grows
     float best = -INFINITY, zr = 0.f;
@@ -1662,23 +1644,34 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     // R3: TV between the MX row and the reference row, and the P path
     float tv = 0.f, pz = 0.f, tvp = 0.f, psum = 0.f;
     const float offm = kOff - rc_m(), invz = 1.f / rc_z();
+    // TV: the reference K tiles once more through the load ring
+    issue_from(rkr, 0);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int j0 = kbase + t * 16;
+      if (j0 < kmax) {
+        float u[4];
+        ref_tile(opaque(t), u);  // (a run-time tile index: its load addresses are formed here, not kept live)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pm = __builtin_amdgcn_exp2f(fmaxf(scr(t, i) + offm, -256.f)) * invz;
+          tv += fabsf(pm - __builtin_amdgcn_exp2f(u[i] - mref) * invZr);
+        }
+      }
+      tv = opaque(tv);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // a tile issued past this wave's last visible key has landed
+    // the P path: per 32-key block (tiles t, t+1; TPW is even in MX mode) of the MX row
 #pragma unroll
     for (int t = 0; t < TPW; t += 2) {
       const int j0 = kbase + t * 16;
       if (j0 < kmax) {
       float pv[2][4];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        float u[4];
-        ref_tile_direct(j0 + 16 * h2, u);
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pm = __builtin_amdgcn_exp2f(fmaxf(scr(t + h2, i) + offm, -256.f)) * invz;
-          pv[h2][i] = pm;
-          tv += fabsf(pm - __builtin_amdgcn_exp2f(u[i] - mref) * invZr);
-        }
-      }
-      // one 32-key block: keys j0 .. j0+31 (tiles t, t+1)
+        for (int i = 0; i < 4; ++i) pv[h2][i] = __builtin_amdgcn_exp2f(fmaxf(scr(t + h2, i) + offm, -256.f)) * invz;
       float amax = 0.f;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
