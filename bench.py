@@ -675,7 +675,7 @@ def run_p2(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "kvprof runs on one GPU per process; --gpus must be 1"}))
         sys.exit(2)
     import torch
 

@@ -53,7 +53,7 @@ extern "C" {
 #define KVPROF_ESHAPE (-2)      /* inconsistent or unsupported dimensions                          */
 #define KVPROF_EALIGN (-3)      /* pointer not aligned as the argument requires                    */
 #define KVPROF_ESIZE (-4)       /* an output or workspace buffer is too small                      */
-#define KVPROF_EUNSUPPORTED (-6)/* valid request outside what this build implements                */
+#define KVPROF_EUNSUPPORTED (-6)/* valid request outside what the library implements                */
 #define KVPROF_ELAUNCH (-7)     /* the HIP runtime rejected a kernel launch                        */
 
 /* Score sources of kvprof_row_stats / kvprof_attend. */
@@ -61,7 +61,7 @@ extern "C" {
 #define KVPROF_MODE_MXFP8 1  /* MXFP8 Q and K codes (from kvprof_pack_mxfp8); bf16 Q, K = reference  */
 #define KVPROF_MODE_INT4KV 2 /* bf16 Q against packed 4-bit K/V blobs (from kvprof_pack_int4kv)     */
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define KVPROF_HEAD_DIM 128      /* head dimension of the full statistics (32 and 64: see attend)    */
 #define KVPROF_MAX_KEYS 6272     /* keys per row held on chip by one workgroup (8 waves x 49 tiles)  */
 #define KVPROF_MAX_KEYS_MX 6400  /* keys per row in MXFP8 mode (8 waves x 50 tiles)                    */

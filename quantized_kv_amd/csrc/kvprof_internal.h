@@ -85,7 +85,7 @@ hipError_t launch_row_stats(const RowStatsParams& p, int tpw, int ksrc, bool mx,
 hipError_t launch_row_stats_bf16(const RowStatsParams& p, int tpw, hipStream_t s);
 hipError_t launch_row_stats_int4(const RowStatsParams& p, int tpw, hipStream_t s);
 hipError_t launch_row_stats_mx(const RowStatsParams& p, int tpw, hipStream_t s);
-int row_stats_tpw_for(int n_k, bool mx);  // tiles per wave this build uses for n_k keys, or -1
+int row_stats_tpw_for(int n_k, bool mx);  // tiles per wave the library uses for n_k keys, or -1
 
 hipError_t launch_heatmap(const float* frame_mass, const int* row_group, int n_batch, int hq,
                           int nq, int n_groups, int n_frames, float* heatmap, float* heatmap_mean,
