@@ -260,3 +260,35 @@ def test_mxfp8_blocks_below_bf16_range(kvprof_lib):
     _check_zero_frac(g["p_zero_frac"], ref["p"], Sk)
     _check_argmax(g["argmax"], ref["scores"], "argmax")
     _check_argmax(g["argmax_ref"], ref["ref_scores"], "argmax_ref")
+
+
+def test_mxfp8_ragged_gqa_bias(kvprof_lib):
+    """MXFP8 mode with ragged shapes: 45 rows per head (the last 16-row block a third full), 1,000 keys
+    (the last 16-key tile half full, so the reference sweeps stop inside a wave's range), GQA 4/2, a
+    random key bias, three regions and eight frames; every row of every head against the oracle."""
+    Bn, Hq, Hkv, Mq, Sk = 1, 4, 2, 45, 1000
+    Q, K, _ = inputs.generic_inputs(37, (Bn, Hq, Mq, 128), (Bn, Hkv, Sk, 128), q_scale=1.3)
+    bias = (np.random.default_rng(38).standard_normal(Sk) * 0.6).astype(np.float32)
+    signs = inputs.hadamard_signs(4)
+    sg = torch.from_numpy(signs).to(DEV)
+    qd, kd = Q.to(DEV), K.to(DEV)
+    print("MXFP8 ragged GQA", flush=True)
+    qc, qs = B.kvprof_pack_mxfp8(qd.reshape(-1, 128), sg)
+    kc, ks = B.kvprof_pack_mxfp8(kd.reshape(-1, 128), sg)
+    kw = dict(region_bounds=[0, 130, 610, Sk], frame_len=125, n_frames=8)
+    want = ("support", "top_mass", "top32", "strict_zero", "region_mass", "frame_mass", "tv_qk", "argmax",
+            "argmax_ref", "p_zero_frac", "tv_p", "p_rowsum")
+    g = _np(B.run(qd, kd, want=want, mode=B.MODE_MXFP8, q_codes=qc, q_scales=qs, k_codes=kc, k_scales=ks,
+                  scale=0.1, key_bias=torch.from_numpy(bias).to(DEV), **kw))
+    torch.cuda.synchronize()
+    qv, kv = inputs.bf16_values(Q)[0], inputs.bf16_values(K)[0]
+    for h in range(Hq):
+        ref = O.mx_row_stats(qv[h], kv[h // 2], signs, scale=0.1, key_bias=bias, **kw)
+        gv = {k: v[h * Mq:(h + 1) * Mq] for k, v in g.items()}
+        P.check_rows(gv, ref)
+        P.check_close("tv_qk", gv["tv_qk"], ref["tv_qk"], atol=P.MASS_ATOL)
+        P.check_close("tv_p", gv["tv_p"], ref["tv_p"], atol=P.MASS_ATOL)
+        P.check_close("p_rowsum", gv["p_rowsum"], ref["p_rowsum"], atol=P.MASS_ATOL)
+        _check_zero_frac(gv["p_zero_frac"], ref["p"], Sk)
+        _check_argmax(gv["argmax"], ref["scores"], "argmax")
+        _check_argmax(gv["argmax_ref"], ref["ref_scores"], "argmax_ref")
