@@ -406,6 +406,39 @@ __device__ __forceinline__ void load_v8(const RowStatsParams& p, rsrc_t rv, cons
   }
 }
 
+// Raw words of eight V values (channels c0 .. c0+7 of key j), for keys in the 4-bit section (INT4KV:
+// the code word and the (scale, min) word) or any key (BF16: one 16-byte load), and their decode as
+// load_v8 does it. Loaded a few tiles ahead of their use.
+template <int KSRC>
+struct VRaw;
+template <>
+struct VRaw<KSRC_BF16> { u32x4 v; };
+template <>
+struct VRaw<KSRC_INT4> { uint32_t codes, wd; };
+template <int KSRC>
+__device__ __forceinline__ VRaw<KSRC> load_v_raw(rsrc_t rv, const Int4Layout& L, int j, int c0) {
+  VRaw<KSRC> x;
+  if constexpr (KSRC == KSRC_BF16) {
+    x.v = __builtin_amdgcn_raw_buffer_load_b128(rv, (unsigned)(j * KVPROF_HEAD_DIM + c0) * 2u, 0, 0);
+  } else {
+    x.codes = __builtin_amdgcn_raw_buffer_load_b32(rv, (unsigned)(L.vc + (size_t)j * 64 + c0 / 2), 0, 0);
+    x.wd = __builtin_amdgcn_raw_buffer_load_b32(rv, (unsigned)(L.vm + ((size_t)j * 4 + c0 / 32) * 4), 0, 0);
+  }
+  return x;
+}
+template <int KSRC>
+__device__ __forceinline__ void decode_v8(const VRaw<KSRC>& r, _Float16 (&x)[8]) {
+  if constexpr (KSRC == KSRC_BF16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (_Float16)__uint_as_float(((r.v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16);
+  } else {
+    const float s_ = (float)__builtin_bit_cast(_Float16, (uint16_t)(r.wd & 0xFFFF));
+    const float m_ = (float)__builtin_bit_cast(_Float16, (uint16_t)(r.wd >> 16));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (_Float16)fmaf((float)((r.codes >> (4 * e)) & 0xF), s_, m_);
+  }
+}
+
 template <int KSRC>
 __device__ __forceinline__ f32x4 mfma_step(u32x4 a, u32x4 b, f32x4 acc) {
   if (KSRC == KSRC_BF16)
@@ -1494,17 +1527,41 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
       f32x4 oacc[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // V words of a tile are loaded kVPf tiles before their use where the tile is visible and (INT4KV)
+      // inside the 4-bit section; other tiles (the float32 window) load at their use. Rows of more than
+      // 40 tiles per wave have no registers to spare for it.
+      constexpr int kVPf = 2;
+      constexpr bool kVOn = TPW <= 40;
+      auto vpre = [&](int t) {
+        const int jt = kbase + t * 16;
+        return kVOn && jt < kmax && (KSRC == KSRC_BF16 || jt + 16 <= (int)L.n);
+      };
+      VRaw<KSRC> vraw[kVPf][2];
+#pragma unroll
+      for (int t = 0; t < kVPf && t < TPW; ++t)
+        if (vpre(t))
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+            vraw[t][kk] = load_v_raw<KSRC>(rv, L, kbase + t * 16 + 2 * kp + kk, half * 64 + 8 * q8);
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int j0 = kbase + t * 16;
         if (j0 < kmax) {
+          const bool pre = vpre(t);
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk) {  // one key at a time (the scores are live in registers)
             _Float16 x[8];
-            load_v8<KSRC>(p, rv, L, j0 + 2 * kp + kk, half * 64 + 8 * q8, x);
+            if (pre)
+              decode_v8<KSRC>(vraw[t % kVPf][kk], x);
+            else
+              load_v8<KSRC>(p, rv, L, j0 + 2 * kp + kk, half * 64 + 8 * q8, x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) sm.u.vst[w][8 * q8 + e][2 * kp + kk] = x[e];
           }
+          if (t + kVPf < TPW && vpre(t + kVPf))
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+              vraw[t % kVPf][kk] = load_v_raw<KSRC>(rv, L, j0 + kVPf * 16 + 2 * kp + kk, half * 64 + 8 * q8);
           f16x4 pa;
 #pragma unroll
           for (int i = 0; i < 4; ++i) pa[i] = (_Float16)(__builtin_amdgcn_exp2f(fmaxf(scr(t, i) + offq, -256.f)) * pm);
