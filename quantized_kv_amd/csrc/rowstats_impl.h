@@ -681,13 +681,36 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
 #pragma unroll
     for (int t = 0; t < kRing - 1 && t < TPW; ++t) issue(t);
   }
-  // Int4 keys of the 4-bit section: the raw words of the next tile are loaded while this one is
-  // decoded and multiplied (for row lengths up to 4,096 keys; longer rows have no registers left).
-  constexpr bool kPf4 = KSRC == KSRC_INT4 && TPW <= 32;
-  K4Raw pf4[4];
-  if (kPf4 && kbase + 16 <= (int)L.n) {
+  // Int4 keys of the 4-bit section reach LDS the same way, kRing4 tiles deep, in the same per-wave
+  // bytes: a slot holds the tile's 16 code rows (64 B each, key-major), the (scale, min) words of its
+  // 32-token group (128 channels x 4 B) and its 16 bias values. Three loads per tile: the codes (all
+  // lanes, 16 B each), the group words (lanes 0..31) and the bias (lanes 0..15). A tile goes through
+  // the ring when it is visible and inside the 4-bit section (tiles never straddle the window: the
+  // section holds whole 32-token groups); float32 window tiles load directly.
+  constexpr int kRing4 = 5;
+  constexpr int kSlot4 = 16 * 64 + 128 * 4 + 16 * 4;  // 1,600 B
+  static_assert(kRing4 * kSlot4 <= (int)sizeof(sm.u.a.ring[0]), "int4 ring slots fit the wave's ring bytes");
+  auto ring4 = [&](int slot) { return reinterpret_cast<char*>(&sm.u.a.ring[w][0][0][0]) + slot * kSlot4; };
+  auto q4 = [&](int t) {  // wave-uniform, and false from the first tile it is false for
+    const int jt = kbase + t * 16;
+    return KSRC == KSRC_INT4 && jt < kmax && jt + 16 <= (int)L.n;
+  };
+  auto issue4 = [&](int t) {
+    const int jt = kbase + t * 16;
+    char* dst = ring4(t % kRing4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)dst, 16,
+                                             (unsigned)(L.kc + (size_t)jt * 64 + lane * 16), 0, 0, 0);
+    if (lane < 32)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dst + 1024), 16,
+                                               (unsigned)(L.km + ((size_t)(jt >> 5) * 128 + 4 * lane) * 4), 0, 0, 0);
+    if (lane < 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (__attribute__((address_space(3))) void*)(dst + 1536), 4,
+                                               (unsigned)(jt + lane) * 4u, 0, 0, 0);
+  };
+  if (KSRC == KSRC_INT4) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) pf4[ks] = load_k4_raw(rk, L, kbase + r, ks * 32 + 8 * g);
+    for (int t = 0; t < kRing4 - 1 && t < TPW; ++t)
+      if (q4(t)) issue4(t);
   }
   // bf16 keys: this lane's Q fragments stay in registers for the score pass (read from LDS once
   // instead of once per tile: a third of the pass's LDS traffic). The int4 path, whose prefetched raw
@@ -715,20 +738,38 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
           acc = mfma_step<KSRC>(sm.u.a.ring[w][t % kRing][r >> 2][(r & 3) * 16 + ((4 * ks + g) ^ r)], qfr[ks], acc);
       }
       bias = *reinterpret_cast<const f32x4*>(&sm.u.a.rbias[w][t % kRing][4 * g]);
+    } else if (q4(t)) {
+      // wave-uniform: the tile's codes, group words and bias are in ring slot t % kRing4; the three
+      // loads of each later tile in the ring may still be outstanding
+      if (t + kRing4 - 1 < TPW && q4(t + kRing4 - 1)) {
+        issue4(t + kRing4 - 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * (kRing4 - 1)));
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      const char* src = ring4(t % kRing4);
+      u32x4 kf[4], kl[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        K4Raw kr;
+        kr.codes = *reinterpret_cast<const uint32_t*>(src + r * 64 + ks * 16 + 4 * g);
+        kr.m0 = *reinterpret_cast<const u32x4*>(src + 1024 + (ks * 32 + 8 * g) * 4);
+        kr.m1 = *reinterpret_cast<const u32x4*>(src + 1024 + (ks * 32 + 8 * g) * 4 + 16);
+        kf[ks] = decode_k4(kr, kl[ks]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        acc = mfma_step<KSRC>(kf[ks], sm.qs[r][ks * 4 + g], acc);
+        acc = mfma_step<KSRC>(kl[ks], sm.qs[r][ks * 4 + g], acc);
+      }
+      bias = *reinterpret_cast<const f32x4*>(src + 1536 + 16 * g);
     } else {
+      // float32 window tiles (after every ring tile of this wave has been consumed) and tiles past the
+      // visible keys
       if (j0 < kmax) {
         u32x4 kf[4], kl[4];
-        if (kPf4 && j0 + 16 <= (int)L.n) {  // wave-uniform: this tile's raw words were loaded a tile ago
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) kf[ks] = decode_k4(pf4[ks], kl[ks]);
-        } else {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) kf[ks] = load_k<KSRC>(p, rk, L, j0 + r, ks * 32 + 8 * g, &kl[ks]);
-        }
-        if (kPf4 && t + 1 < TPW && j0 + 32 <= (int)L.n) {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) pf4[ks] = load_k4_raw(rk, L, j0 + 16 + r, ks * 32 + 8 * g);
-        }
+        for (int ks = 0; ks < 4; ++ks) kf[ks] = load_k<KSRC>(p, rk, L, j0 + r, ks * 32 + 8 * g, &kl[ks]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           acc = mfma_step<KSRC>(kf[ks], sm.qs[r][ks * 4 + g], acc);
@@ -776,7 +817,7 @@ __global__ __launch_bounds__(WGT) void row_kernel(const RowStatsParams p) {
     usum = opaque(usum);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (KSRC == KSRC_BF16) __builtin_amdgcn_s_waitcnt(0x0F70);  // every ring load has landed
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // every ring load has landed
   umax = row_max4(umax);
   umin = row_min4(umin);
   usum = row_sum4(usum);
