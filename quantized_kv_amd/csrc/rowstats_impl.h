@@ -350,19 +350,11 @@ __device__ __forceinline__ u32x4 load_k(const RowStatsParams& p, rsrc_t rk, cons
 }
 
 // Int4 K of a key inside the 4-bit section, from its raw words (as load_k decodes them): the code
-// word of dims d0 .. d0+7 and their (scale, min) pairs.
+// word of dims d0 .. d0+7 and their (scale, min) pairs, read from the LDS load ring.
 struct K4Raw {
   uint32_t codes;
   u32x4 m0, m1;
 };
-__device__ __forceinline__ K4Raw load_k4_raw(rsrc_t rk, const Int4Layout& L, int ja, int d0) {
-  K4Raw k;
-  k.codes = __builtin_amdgcn_raw_buffer_load_b32(rk, (unsigned)(L.kc + (size_t)ja * 64 + d0 / 2), 0, 0);
-  const unsigned mo = (unsigned)(L.km + ((size_t)(ja >> 5) * 128 + d0) * 4);
-  k.m0 = __builtin_amdgcn_raw_buffer_load_b128(rk, mo, 0, 0);
-  k.m1 = __builtin_amdgcn_raw_buffer_load_b128(rk, mo + 16u, 0, 0);
-  return k;
-}
 __device__ __forceinline__ u32x4 decode_k4(const K4Raw& k, u32x4& lo_out) {
   f16x8 h, hl;
 #pragma unroll
