@@ -147,3 +147,19 @@ def test_rolling_token_by_token_decode(kvprof_lib):
             assert torch.equal(blob, one), n
             assert torch.equal(a["o"], b["o"]), n
             assert n + 1 < R + 32 or R <= r < R + 32
+
+
+def test_p2_batched_equals_per_input(kvprof_lib):
+    """The batched runner (the inputs of one length in the batch dimension of each call) gives exactly the
+    per-input runner's relative L2 and recent-window mass for every input and window."""
+    print("P2 batched vs per input", flush=True)
+    for n in inputs.P2_LENGTHS:
+        keys = [(variant, seed) for variant in inputs.TINY_VARIANTS for seed in inputs.P2_SEEDS]
+        qkv = [inputs.p2_inputs(seed, n, variant) for variant, seed in keys]
+        q, k, v = (torch.stack([t[j] for t in qkv]).to(DEV) for j in range(3))
+        batched = p2.run_batch(q, k, v)
+        for i, (variant, seed) in enumerate(keys):
+            one = p2.run_case(q[i], k[i], v[i])
+            for r in inputs.P2_WINDOWS:
+                assert batched[i]["rel_l2"][r] == one["rel_l2"][r], (n, variant, seed, r)
+                assert abs(batched[i]["recent_mass"][r] - one["recent_mass"][r]) <= 1e-12, (n, variant, seed, r)
