@@ -11,6 +11,37 @@ namespace kvp {
 namespace {
 
 // One thread per (batch, head, group, frame): mean over the rows of that group, in row order.
+// One workgroup per (batch, query head) when n_groups * n_frames <= 256: the head's frame masses and
+// the rows' groups pass through LDS in chunks of 128 rows, and thread (group, frame) adds its group's
+// rows in row order, the same order as heatmap_kernel (so the same sums).
+constexpr int kHmChunk = 128;
+__global__ __launch_bounds__(256) void heatmap_block_kernel(const float* __restrict__ fm, const int* __restrict__ row_group,
+                                                            int nq, int ng, int nf, float* __restrict__ hm) {
+  __shared__ float tile[kHmChunk * KVPROF_MAX_FRAMES];
+  __shared__ int tg[kHmChunk];
+  const long long bh = blockIdx.x;
+  const float* base = fm + bh * (long long)nq * nf;
+  const int t = threadIdx.x;
+  const bool act = t < ng * nf;
+  const int gq = act ? t / nf : 0, f = act ? t - gq * nf : 0;
+  float s = 0.f;
+  int cnt = 0;
+  for (int i0 = 0; i0 < nq; i0 += kHmChunk) {
+    const int nr = min(kHmChunk, nq - i0);
+    __syncthreads();  // the previous chunk has been read
+    for (int e = t; e < nr * nf; e += blockDim.x) tile[e] = base[(long long)i0 * nf + e];
+    for (int e = t; e < nr; e += blockDim.x) tg[e] = row_group[i0 + e];
+    __syncthreads();
+    if (act)
+      for (int i = 0; i < nr; ++i)
+        if (tg[i] == gq) {
+          s += tile[i * nf + f];
+          ++cnt;
+        }
+  }
+  if (act) hm[bh * ng * nf + t] = cnt ? s / (float)cnt : 0.f;
+}
+
 __global__ void heatmap_kernel(const float* __restrict__ fm, const int* __restrict__ row_group,
                                int n_batch, int hq, int nq, int ng, int nf, float* __restrict__ hm) {
   long long total = (long long)n_batch * hq * ng * nf;
@@ -154,8 +185,12 @@ hipError_t launch_heatmap(const float* frame_mass, const int* row_group, int n_b
                           hipStream_t s) {
   long long n = (long long)n_batch * hq * n_groups * n_frames;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(heatmap_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, frame_mass, row_group,
-                     n_batch, hq, nq, n_groups, n_frames, heatmap);
+  if ((long long)n_groups * n_frames <= 256)
+    hipLaunchKernelGGL(heatmap_block_kernel, dim3((unsigned)((long long)n_batch * hq)), dim3(256), 0, s, frame_mass,
+                       row_group, nq, n_groups, n_frames, heatmap);
+  else
+    hipLaunchKernelGGL(heatmap_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, frame_mass, row_group,
+                       n_batch, hq, nq, n_groups, n_frames, heatmap);
   if (heatmap_mean) {
     long long m = (long long)n_batch * n_groups * n_frames;
     hipLaunchKernelGGL(heatmap_mean_kernel, dim3(grid_for(m, 256)), dim3(256), 0, s, heatmap, n_batch,
